@@ -1,0 +1,169 @@
+"""Python access to the CPU oracle (oracle_gemm.c).
+
+TEST INFRASTRUCTURE ONLY: the plain fp64 reference that the GPU library is
+checked against.  Only the test suite, the smoke check and the CPU-baseline leg
+of the benchmark may import this package; the GPU library never does, and this
+package imports nothing from it.
+
+`build()` compiles oracle_gemm.c with gcc (no HIP, no BLAS, no fast-math, no
+FMA contraction) into liboracle.so next to this file.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_gemm.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_TYPE = {np.dtype(np.float32): 0, np.dtype(np.float16): 1, np.dtype(np.float64): 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle.  Called by the project's build step."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-pthread", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def bind(path: str):
+    """Load an oracle shared library and declare its entry points."""
+    lib = ctypes.CDLL(path)
+    i64, dbl, vp, ci = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+    lib.oracle_gemm.argtypes = [ci, ci, i64, i64, i64, dbl, vp, i64, ci, vp, i64, ci,
+                                dbl, vp, i64, ci, vp, vp, ci]
+    lib.oracle_gemm.restype = ci
+    lib.oracle_gemm_points.argtypes = [ci, ci, i64, i64, i64, dbl, vp, i64, ci, vp, i64, ci,
+                                       dbl, vp, i64, ci, i64, vp, vp, vp, vp, ci]
+    lib.oracle_gemm_points.restype = ci
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = dbl
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = bind(_LIB)
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(a, name):
+    if a is None:
+        return
+    if a.dtype not in _TYPE:
+        raise TypeError(f"{name}: unsupported dtype {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError(f"{name} must be C-contiguous (row stride is passed as ld)")
+
+
+def gemm(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float, A: np.ndarray, lda: int,
+         B: np.ndarray, ldb: int, beta: float, C0: np.ndarray | None, ldc: int,
+         nthreads: int = 0, want_abs: bool = True):
+    """Full oracle result.  A, B, C0 are the *stored* buffers (fp32, fp16 or
+    fp64, C-contiguous, row stride lda/ldb/ldc).  Returns (ref, absum) as fp64
+    M x N arrays (absum is None when want_abs is False)."""
+    lib = _load()
+    for a, n in ((A, "A"), (B, "B"), (C0, "C0")):
+        _check(a, n)
+    ref = np.empty((M, N), dtype=np.float64)
+    absum = np.empty((M, N), dtype=np.float64) if want_abs else None
+    tc = _TYPE[C0.dtype] if C0 is not None else 2
+    rc = lib.oracle_gemm(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda,
+                         _TYPE[A.dtype], _ptr(B), ldb, _TYPE[B.dtype], float(beta), _ptr(C0), ldc,
+                         tc, ref.ctypes.data, _ptr(absum), int(nthreads))
+    if rc < 0:
+        raise RuntimeError(f"oracle_gemm failed ({rc})")
+    return ref, absum
+
+
+def gemm_points(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float, A, lda, B, ldb,
+                beta: float, C0, ldc, rows: np.ndarray, cols: np.ndarray, nthreads: int = 0):
+    """Oracle value and absum at the elements (rows[p], cols[p])."""
+    lib = _load()
+    for a, n in ((A, "A"), (B, "B"), (C0, "C0")):
+        _check(a, n)
+    pi = np.ascontiguousarray(rows, dtype=np.int64)
+    pj = np.ascontiguousarray(cols, dtype=np.int64)
+    ref = np.empty(pi.shape[0], dtype=np.float64)
+    absum = np.empty(pi.shape[0], dtype=np.float64)
+    tc = _TYPE[C0.dtype] if C0 is not None else 2
+    rc = lib.oracle_gemm_points(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda,
+                                _TYPE[A.dtype], _ptr(B), ldb, _TYPE[B.dtype], float(beta),
+                                _ptr(C0), ldc, tc, pi.shape[0], pi.ctypes.data, pj.ctypes.data,
+                                ref.ctypes.data, absum.ctypes.data, int(nthreads))
+    if rc < 0:
+        raise RuntimeError(f"oracle_gemm_points failed ({rc})")
+    return ref, absum
+
+
+def f16_to_f64(bits: int) -> float:
+    return _load().oracle_f16_to_f64(bits)
+
+
+# ---------------------------------------------------------------------------
+# Error bound of the comparison
+# ---------------------------------------------------------------------------
+RTOL = {"f32": 2e-5, "f16": 2e-3}
+ATOL = {"f32": 1e-6, "f16": 1e-4}
+
+
+def half_ulp_f16(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of fp16 numbers at |x| (the rounding of an fp16 output).
+    Beyond the largest finite fp16 the output overflows; the bound is then
+    infinite and the comparison is made on the infinity itself."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = np.abs(ax.astype(np.float16))
+        sp = np.spacing(h).astype(np.float64)
+    sp = np.where(np.isfinite(sp), sp, np.inf)
+    return 0.5 * sp
+
+
+def bound(dtype: str, ref, absum, alpha: float, beta: float, c0_logical=None) -> np.ndarray:
+    """|C - ref| <= rtol * (|alpha| * absum + |beta * C0|) + atol (+ fp16 half-ulp).
+
+    The stated bound is rtol * sum_k |a_ik b_kj| + atol at alpha=1, beta=0;
+    with general alpha and beta the sum is scaled by |alpha| and the C0 term
+    |beta * C0| is added.  fp16 outputs are additionally allowed half an fp16
+    ulp of the reference (their final rounding)."""
+    extra = 0.0
+    if beta != 0.0 and c0_logical is not None:
+        extra = np.abs(beta * np.asarray(c0_logical, dtype=np.float64))
+    b = RTOL[dtype] * (abs(alpha) * np.asarray(absum) + extra) + ATOL[dtype]
+    if dtype == "f16":
+        b = b + half_ulp_f16(ref)
+    return b
+
+
+def compare(dtype: str, got, ref, absum, alpha: float, beta: float, c0_logical=None):
+    """Returns (max err/bound, number of violations).  NaN in `got` counts as a
+    violation; an infinity passes only where the reference rounds to the same
+    infinity in the output type."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    b = bound(dtype, ref, absum, alpha, beta, c0_logical)
+    with np.errstate(invalid="ignore", over="ignore"):
+        err = np.abs(got - ref)
+        inf_ok = np.isinf(got) & np.isinf(b)
+        if dtype == "f16":
+            inf_ok &= (np.sign(got) == np.sign(ref))
+        ratio = np.where(inf_ok, 0.0, err / b)
+    ratio = np.where(np.isnan(ratio), np.inf, ratio)
+    bad = int(np.count_nonzero(ratio > 1.0))
+    return (float(ratio.max()) if ratio.size else 0.0), bad
