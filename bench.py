@@ -1,0 +1,179 @@
+"""Benchmark of the dense GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+A step is one C = A @ B in fp32, M = N = K = 4096, row-major, not transposed,
+A and B iid uniform[-1, 1) (seed 1), already resident in device memory; the
+timed region is exactly K steps on one stream, bracketed by device
+synchronisation.  Also measured (same method, extra keys of the one JSON
+line): fp16 operands / fp32 accumulation / fp16 output at 2048^3 in the nn,
+tn and nt variants (entries N(0,1)/sqrt(K) rounded to fp16, seed 2).
+
+`roofline` is for the fp32 kernel: achieved TFLOP/s = 2*M*N*K per launch /
+mean launch duration, timed with events recorded on the stream the kernel runs
+on, against the MI355X dense fp32 matrix peak (157.3 TFLOP/s).  `cpu_baseline`
+times the CPU oracle (plain fp64 triple loop, all host cores) on a bounded
+sample of the same workload: whole rows of C.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix
+PEAK_F16 = 2516.6     # TFLOP/s, MI355X dense fp16 matrix
+HBM_PEAK = 8000.0     # GB/s
+
+
+def tflops(M, N, K, seconds):
+    return 2.0 * M * N * K / seconds / 1e12
+
+
+def time_launches(fn, stream, reps):
+    """Mean duration of one launch (s), from events on `stream` around reps launches."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-f16", action="store_true", help="skip the fp16 2048^3 measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the library is a single-GPU kernel library)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dense_gemm_amd as dg
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    # ---- fp32 4096^3 nn ---------------------------------------------------
+    M = N = K = 4096
+    a, b, _ = synth.problem(M, N, K, "f32", "uniform", 1)
+    A = torch.from_numpy(a).to(dev)
+    B = torch.from_numpy(b).to(dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    kernel = dg.dg_select_kernel(0, 0, M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N,
+                                 dg.DG_F32)
+
+    def step():
+        rc = dg.dg_gemm(0, 0, M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N, 0.0, C.data_ptr(),
+                        N, dg.DG_F32, sptr)
+        if rc != 0:
+            raise dg.GemmError(rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    launch_s = time_launches(step, stream, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    value = tflops(M, N, K, wall / args.steps)
+    achieved = tflops(M, N, K, launch_s)
+
+    out = {
+        "metric": "TFLOP/s + % of MFMA peak: fp32 4096^3 nn; fp16->fp32 2048^3 nn/tn/nt",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (uniform[-1,1) fp32, seed 1, SplitMix64)",
+        "config": {"workload": "SGEMM fp32 row-major nn M=N=K=4096 alpha=1 beta=0",
+                   "M": M, "N": N, "K": K, "kernel": dg.dg_kernel_name(kernel)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32, 4), "traffic": None,
+                     "algorithmic_bytes": 3 * M * N * 4, "kernel_ms": round(launch_s * 1e3, 4)},
+    }
+
+    # ---- fp16 2048^3 nn / tn / nt ---------------------------------------------
+    if not args.no_f16:
+        S = 2048
+        a16, b16, _ = synth.problem(S, S, S, "f16", "normal_sqrtk", 2)
+        res = {}
+        for name, ta, tb in (("nn", 0, 0), ("tn", 1, 0), ("nt", 0, 1)):
+            As = torch.from_numpy(np.ascontiguousarray(a16.T if ta else a16)).to(dev)
+            Bs = torch.from_numpy(np.ascontiguousarray(b16.T if tb else b16)).to(dev)
+            Cs = torch.empty((S, S), dtype=torch.float16, device=dev)
+            k16 = dg.dg_select_kernel(ta, tb, S, S, S, As.data_ptr(), S, Bs.data_ptr(), S,
+                                      Cs.data_ptr(), S, dg.DG_F16_F32ACC)
+
+            def step16(ta=ta, tb=tb, As=As, Bs=Bs, Cs=Cs):
+                rc = dg.dg_gemm(ta, tb, S, S, S, 1.0, As.data_ptr(), S, Bs.data_ptr(), S, 0.0,
+                                Cs.data_ptr(), S, dg.DG_F16_F32ACC, sptr)
+                if rc != 0:
+                    raise dg.GemmError(rc)
+
+            for _ in range(20):
+                step16()
+            torch.cuda.synchronize()
+            reps = max(args.steps, 200)
+            t16 = min(time_launches(step16, stream, reps) for _ in range(3))
+            ach = tflops(S, S, S, t16)
+            res[name] = {"tflops": round(ach, 2), "frac": round(ach / PEAK_F16, 4),
+                         "kernel_us": round(t16 * 1e6, 2), "kernel": dg.dg_kernel_name(k16)}
+        out["fp16_2048"] = {"peak": PEAK_F16, "unit": "TFLOP/s", **res}
+
+    # ---- CPU baseline: the oracle on whole rows of the same problem -------------
+    if not args.no_cpu:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+
+        def oracle_rows(nrows):
+            t = time.perf_counter()
+            ref, ab = oracle.gemm(False, False, nrows, N, K, 1.0, a[:nrows], K, b, N, 0.0, None,
+                                  N, nthreads=cores)
+            return time.perf_counter() - t, ref, ab
+
+        t_probe, _, _ = oracle_rows(cores)              # one row per thread
+        nrows = cores * int(max(1, min(M // cores, args.cpu_seconds / max(t_probe, 1e-6))))
+        t_cpu, ref, ab = oracle_rows(nrows)
+        got = C[:nrows].cpu().numpy().astype(np.float64)
+        worst, bad = oracle.compare("f32", got, ref, ab, 1.0, 0.0)
+        flops = 2.0 * nrows * N * K
+        out["cpu_baseline"] = {"value": round(flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": cores, "kind": "oracle",
+                               "sample": f"rows 0..{nrows - 1} of C (all {N} columns, K={K}), "
+                                         f"{t_cpu:.1f} s",
+                               "sample_max_err_over_bound": round(worst, 4),
+                               "sample_violations": bad}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+// Host side of libdense_gemm_amd.so: argument validation, the kernel table,
+// kernel selection and launch on the caller's stream.  The C ABI is declared
+// in include/dense_gemm.h.
+#include "../../include/dense_gemm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.hpp"
+
+namespace dg {
+launch_fn simple_launcher(int dtype, int ta, int tb);
+launch_fn scale_launcher(int dtype);
+const launch_fn *f32_launchers(int config);
+const launch_fn *f16_launchers(int config);
+}  // namespace dg
+
+namespace {
+
+using dg::GemmParams;
+using dg::launch_fn;
+
+thread_local int g_last_hip_error = 0;
+
+// One entry per compiled kernel family.  Matrix-core families come in 8
+// variants: transA x transB x (16-byte vector loads or element loads).
+struct Family {
+    const char *name;
+    int dtype;
+    int bm, bn;
+    int group_m;
+    bool mfma;
+    const launch_fn *(*variants)(int);  // mfma: table(config)[vec ? 0 : 4 + ta*2 + tb]
+    int config;
+};
+
+const Family kFamilies[] = {
+    {"f32_64x64_simple", DG_F32, 64, 64, 1, false, nullptr, 0},
+    {"f16_64x64_simple", DG_F16_F32ACC, 64, 64, 1, false, nullptr, 0},
+    {"f32_256x128_mfma32x32x2", DG_F32, 256, 128, 8, true, dg::f32_launchers, 0},
+    {"f32_128x128_mfma32x32x2", DG_F32, 128, 128, 8, true, dg::f32_launchers, 1},
+    {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, true, dg::f16_launchers, 0},
+    {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, true, dg::f16_launchers, 1},
+};
+constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
+enum { K_F32_SIMPLE = 0, K_F16_SIMPLE = 1, K_F32_256 = 2, K_F32_128 = 3, K_F16_128 = 4, K_F16_256 = 5 };
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+int64_t max1(int64_t x) { return x > 1 ? x : 1; }
+
+// Argument checks in parameter order; returns 0 or -(1-based index).
+// check_ptrs = false skips the NULL checks (kernel selection only looks at
+// shapes, strides and alignment).
+int validate(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+             int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc, int dtype,
+             bool check_ptrs = true)
+{
+    if (ta != DG_OP_N && ta != DG_OP_T) return -1;
+    if (tb != DG_OP_N && tb != DG_OP_T) return -2;
+    if (M < 0 || M > kMaxDim) return -3;
+    if (N < 0 || N > kMaxDim) return -4;
+    if (K < 0 || K > kMaxDim) return -5;
+    const bool reads_ab = check_ptrs && M > 0 && N > 0 && K > 0 && alpha != 0.f;
+    if (reads_ab && A == nullptr) return -7;
+    if (lda < max1(ta == DG_OP_T ? M : K)) return -8;
+    if (reads_ab && B == nullptr) return -9;
+    if (ldb < max1(tb == DG_OP_T ? K : N)) return -10;
+    if (check_ptrs && M > 0 && N > 0 && C == nullptr) return -12;
+    if (ldc < max1(N)) return -13;
+    if (dtype != DG_F32 && dtype != DG_F16_F32ACC) return -14;
+    return 0;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// 16-byte vector loads need every row start of A and B on a 16-byte boundary.
+bool vec_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype)
+{
+    const int64_t v = dtype == DG_F32 ? 4 : 8;
+    return aligned16(A) && aligned16(B) && lda % v == 0 && ldb % v == 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Kernel choice by dtype and output tile count.  Larger tiles re-read less
+// of A and B; smaller tiles fill more of the 256 compute units.
+int choose(int64_t M, int64_t N, int dtype)
+{
+    if (dtype == DG_F32) {
+        const int64_t big = ceil_div(M, 256) * ceil_div(N, 128);
+        return big >= 384 ? K_F32_256 : K_F32_128;
+    }
+    const int64_t big = ceil_div(M, 256) * ceil_div(N, 128);
+    return big >= 512 ? K_F16_256 : K_F16_128;
+}
+
+bool supports(int kernel, int dtype, int64_t M, int64_t N)
+{
+    if (kernel < 0 || kernel >= kNumKernels) return false;
+    const Family &f = kFamilies[kernel];
+    if (f.dtype != dtype) return false;
+    if (!f.mfma) return ceil_div(M, 64) <= 65535 && ceil_div(N, 64) <= 0x7fffffff;
+    return ceil_div(M, f.bm) * ceil_div(N, f.bn) <= 0x7fffffff;
+}
+
+int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+        const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype, void *stream,
+        int kernel)
+{
+    int rc = validate(ta, tb, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return DG_OK;
+    if (kernel != DG_KERNEL_AUTO && (kernel < 0 || kernel >= kNumKernels))
+        return DG_ERR_UNSUPPORTED;
+
+    GemmParams p;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.tiles_m = p.tiles_n = 0;
+    p.group_m = 1;
+    hipStream_t s = (hipStream_t)stream;
+    const int di = dtype == DG_F32 ? 0 : 1;
+
+    hipError_t err;
+    if (K == 0 || alpha == 0.f) {
+        err = dg::scale_launcher(di)(p, s);
+    } else {
+        if (kernel == DG_KERNEL_AUTO) kernel = choose(M, N, dtype);
+        if (!supports(kernel, dtype, M, N)) return DG_ERR_UNSUPPORTED;
+        const Family &f = kFamilies[kernel];
+        if (!f.mfma) {
+            err = dg::simple_launcher(di, ta, tb)(p, s);
+        } else {
+            p.tiles_m = (int32_t)ceil_div(M, f.bm);
+            p.tiles_n = (int32_t)ceil_div(N, f.bn);
+            p.group_m = f.group_m;
+            const int v = vec_ok(A, lda, B, ldb, dtype) ? 0 : 4;
+            err = f.variants(f.config)[v + ta * 2 + tb](p, s);
+        }
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return DG_ERR_HIP;
+    }
+    return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+            int64_t lda, const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype,
+            void *stream)
+{
+    return run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
+               DG_KERNEL_AUTO);
+}
+
+int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
+                        void *C, int64_t ldc, int dtype, void *stream, int kernel)
+{
+    return run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
+               kernel);
+}
+
+int dg_select_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+                     int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
+                     int dtype)
+{
+    int rc = validate(transA, transB, M, N, K, 1.f, A, lda, B, ldb, C, ldc, dtype, false);
+    if (rc) return rc;
+    return choose(M, N, dtype);
+}
+
+int dg_kernel_count(void) { return kNumKernels; }
+
+const char *dg_kernel_name(int kernel)
+{
+    return (kernel >= 0 && kernel < kNumKernels) ? kFamilies[kernel].name : nullptr;
+}
+
+int dg_kernel_tile_m(int kernel)
+{
+    return (kernel >= 0 && kernel < kNumKernels) ? kFamilies[kernel].bm : -1;
+}
+
+int dg_kernel_tile_n(int kernel)
+{
+    return (kernel >= 0 && kernel < kNumKernels) ? kFamilies[kernel].bn : -1;
+}
+
+const char *dg_status_string(int status)
+{
+    switch (status) {
+    case DG_OK: return "ok";
+    case DG_ERR_UNSUPPORTED: return "kernel does not support this problem";
+    case DG_ERR_HIP: return "HIP error (see dg_last_hip_error)";
+    case -1: return "invalid transA";
+    case -2: return "invalid transB";
+    case -3: return "invalid M";
+    case -4: return "invalid N";
+    case -5: return "invalid K";
+    case -6: return "invalid alpha";
+    case -7: return "invalid A (NULL)";
+    case -8: return "invalid lda";
+    case -9: return "invalid B (NULL)";
+    case -10: return "invalid ldb";
+    case -11: return "invalid beta";
+    case -12: return "invalid C (NULL)";
+    case -13: return "invalid ldc";
+    case -14: return "invalid dtype";
+    case -15: return "invalid stream";
+    default: return "unknown status";
+    }
+}
+
+int dg_last_hip_error(void) { return g_last_hip_error; }
+
+int dg_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// fp32 matrix-core kernel instantiations (v_mfma_f32_32x32x2_f32).
+#include "gemm_mfma.hpp"
+
+namespace dg {
+
+#define DG_VARIANTS(T, BM, BN, BK, WM, WN, MINW)                                         \
+    {                                                                                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, false, true, MINW>,                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, true, true, MINW>,                    \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, false, true, MINW>,                    \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, true, true, MINW>,                     \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, false, false, MINW>,                  \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, true, false, MINW>,                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, false, false, MINW>,                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, true, false, MINW>,                    \
+    }
+
+// [config][vec ? 0 : 4 + transA * 2 + transB]
+const launch_fn *f32_launchers(int config)
+{
+    static const launch_fn table[2][8] = {
+        DG_VARIANTS(float, 256, 128, 16, 128, 64, 2),
+        DG_VARIANTS(float, 128, 128, 16, 64, 64, 2),
+    };
+    return table[config];
+}
+
+}  // namespace dg

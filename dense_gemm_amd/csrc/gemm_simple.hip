@@ -1,0 +1,155 @@
+// Generic GEMM kernel: any shape, any leading dimension, any alignment, all
+// four transpose pairs, fp32 or fp16 operands, fp32 accumulation.
+//
+// Structure: the shared-memory tiling of "Optimizing GEMM on Apple's M5 from
+// scratch, Part 1" (Kernels 2 and 3: stage a tile of each operand on chip,
+// one barrier after the stores and one before they are overwritten) with the
+// 2x2-per-thread register blocking idea of "From a C loop to a GPU kernel"
+// (GPU tiling section) widened to 4x4, and the zero-filled masked edge loads
+// and guarded stores of that page's tiled kernel.  Each element is loaded on
+// its own, so no alignment is assumed; lanes run along whichever dimension
+// the stored matrix has contiguous.
+//
+// This is the fallback for problems the matrix-core kernels do not take, and
+// it also serves the C = beta*C case (alpha == 0 or K == 0).
+#include "gemm_common.hpp"
+
+namespace dg {
+
+namespace {
+
+constexpr int ST = 64;   // output tile (ST x ST)
+constexpr int SK = 16;   // K slab
+constexpr int SPAD = 4;
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v) { return (float)v; }
+
+template <typename T, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_simple_kernel(GemmParams p)
+{
+    __shared__ float As[SK][ST + SPAD];
+    __shared__ float Bs[SK][ST + SPAD];
+    const T *A = (const T *)p.A;
+    const T *B = (const T *)p.B;
+    T *C = (T *)p.C;
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int m0 = blockIdx.y * ST, n0 = blockIdx.x * ST;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = 0.f;
+
+    for (int k0 = 0; k0 < p.K; k0 += SK) {
+#pragma unroll
+        for (int q = 0; q < (ST * SK) / 256; ++q) {
+            const int e = tid + q * 256;
+            int mm, kk;
+            if (TA) { kk = e / ST; mm = e % ST; }   // stored K x M: lanes along m
+            else    { mm = e / SK; kk = e % SK; }   // stored M x K: lanes along k
+            const int gm = m0 + mm, gk = k0 + kk;
+            float v = 0.f;
+            if (gm < p.M && gk < p.K)
+                v = to_f32(TA ? A[(int64_t)gk * p.lda + gm] : A[(int64_t)gm * p.lda + gk]);
+            As[kk][mm] = v;
+        }
+#pragma unroll
+        for (int q = 0; q < (ST * SK) / 256; ++q) {
+            const int e = tid + q * 256;
+            int nn, kk;
+            if (TB) { nn = e / SK; kk = e % SK; }   // stored N x K: lanes along k
+            else    { kk = e / ST; nn = e % ST; }   // stored K x N: lanes along n
+            const int gn = n0 + nn, gk = k0 + kk;
+            float v = 0.f;
+            if (gn < p.N && gk < p.K)
+                v = to_f32(TB ? B[(int64_t)gn * p.ldb + gk] : B[(int64_t)gk * p.ldb + gn]);
+            Bs[kk][nn] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < SK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int gm = m0 + ty * 4 + i;
+        if (gm >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int gn = n0 + tx * 4 + j;
+            if (gn >= p.N) continue;
+            T *c = C + (int64_t)gm * p.ldc + gn;
+            float v = p.alpha * acc[i][j];
+            if (p.beta != 0.f) v = __builtin_fmaf(p.beta, to_f32(*c), v);
+            *c = (T)v;
+        }
+    }
+}
+
+// C = beta * C over the M x N view (beta == 0 writes zeros without reading C).
+template <typename T>
+__global__ __launch_bounds__(256) void scale_c_kernel(GemmParams p)
+{
+    T *C = (T *)p.C;
+    const int64_t total = (int64_t)p.M * p.N;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e / p.N, j = e - i * p.N;
+        T *c = C + i * p.ldc + j;
+        *c = (p.beta == 0.f) ? (T)0.f : (T)(p.beta * to_f32(*c));
+    }
+}
+
+template <typename T, bool TA, bool TB>
+hipError_t launch_simple(const GemmParams &p, hipStream_t s)
+{
+    dim3 grid((p.N + ST - 1) / ST, (p.M + ST - 1) / ST);
+    hipLaunchKernelGGL((gemm_simple_kernel<T, TA, TB>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scale(const GemmParams &p, hipStream_t s)
+{
+    const int64_t total = (int64_t)p.M * p.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL((scale_c_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// launchers exported to the dispatcher: [dtype][transA][transB]
+launch_fn simple_launcher(int dtype, int ta, int tb)
+{
+    static const launch_fn table[2][2][2] = {
+        {{launch_simple<float, false, false>, launch_simple<float, false, true>},
+         {launch_simple<float, true, false>, launch_simple<float, true, true>}},
+        {{launch_simple<_Float16, false, false>, launch_simple<_Float16, false, true>},
+         {launch_simple<_Float16, true, false>, launch_simple<_Float16, true, true>}},
+    };
+    return table[dtype][ta][tb];
+}
+
+launch_fn scale_launcher(int dtype)
+{
+    return dtype == 0 ? launch_scale<float> : launch_scale<_Float16>;
+}
+
+}  // namespace dg

@@ -1,0 +1,124 @@
+/*
+ * dense_gemm.h -- C ABI of libdense_gemm_amd.so, a dense matrix multiply for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one call):
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * the full SGEMM form given in "Optimizing GEMM on Apple's M5 from scratch,
+ * Part 1", Introduction (whose own runs fix alpha = 1, beta = 0), with the
+ * transpose variants of "Metal GEMM Kernels for LoRA Training on Apple
+ * Silicon", section 2 ("GEMM structure": nn A[M,K] B[K,N], tn A[K,M]^T B[K,N],
+ * nt A[M,K] B[N,K]^T; tt is the remaining combination).
+ *
+ * Layout.  Every matrix is row-major: element (i, j) of a stored matrix X is
+ * X[i * ldX + j] (ld = row stride in elements).  op(A) is M x K and op(B) is
+ * K x N:
+ *   transA = DG_OP_N: A is stored M x K, lda >= max(1, K)
+ *   transA = DG_OP_T: A is stored K x M, lda >= max(1, M)
+ *   transB = DG_OP_N: B is stored K x N, ldb >= max(1, N)
+ *   transB = DG_OP_T: B is stored N x K, ldb >= max(1, K)
+ *   C is stored M x N, ldc >= max(1, N).
+ * A sub-matrix is passed as a pointer to its first element plus the parent's
+ * ld.  Elements outside the logical extents (padding between rows) are never
+ * read and never written.
+ *
+ * Types (dtype):
+ *   DG_F32        A, B, C are fp32; products and sums in fp32 on the fp32
+ *                 matrix cores (full precision, no reduced-precision inputs).
+ *   DG_F16_F32ACC A, B, C are IEEE fp16; products are accumulated in fp32
+ *                 (the fp16 matrix-core path with fp32 accumulators -- "Metal
+ *                 GEMM Kernels for LoRA Training", section 1); the result
+ *                 alpha*acc + beta*C is formed in fp32 (an fp16 C is widened
+ *                 exactly) and rounded once to fp16, round-to-nearest-even,
+ *                 overflow to +-Inf.
+ *   alpha and beta are fp32 for both types.
+ *
+ * Special values of the arguments:
+ *   M == 0 or N == 0       nothing is done (returns DG_OK).
+ *   K == 0 or alpha == 0   C = beta * C; A and B are not read.
+ *   beta == 0              C is write-only: its old contents (NaN included)
+ *                          are not read.
+ *
+ * Pointers, ownership, execution:
+ *   A, B, C are device pointers on the device that `stream` belongs to, owned
+ *   by the caller; the library keeps no reference after the call returns.
+ *   `stream` is a hipStream_t (NULL = the default stream).  The call enqueues
+ *   the work and returns without waiting for it (asynchronous, like any
+ *   kernel launch); it allocates no memory.  Calls are thread-safe.
+ *   C must not overlap A or B (not checked).
+ *
+ * Errors (return value):
+ *   DG_OK (0)          enqueued (or nothing to do).
+ *   -i                 argument i (1-based, in the order of dg_gemm's
+ *                      parameters) is invalid: transA/transB not 0 or 1,
+ *                      M/N/K negative or above 2^31-1, ld below its minimum,
+ *                      NULL pointer with a non-empty extent, unknown dtype.
+ *                      Nothing is enqueued.
+ *   DG_ERR_UNSUPPORTED the forced kernel cannot run this problem.
+ *   DG_ERR_HIP         a HIP call failed; dg_last_hip_error() returns its
+ *                      hipError_t (per calling thread).
+ */
+#ifndef DENSE_GEMM_H
+#define DENSE_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { DG_OP_N = 0, DG_OP_T = 1 };
+enum { DG_F32 = 0, DG_F16_F32ACC = 1 };
+
+#define DG_OK 0
+#define DG_ERR_UNSUPPORTED (-100)
+#define DG_ERR_HIP (-200)
+
+/* Kernel choice for dg_gemm_with_kernel: DG_KERNEL_AUTO lets the library pick. */
+#define DG_KERNEL_AUTO (-1)
+
+/* C = alpha * op(A) * op(B) + beta * C  (see above). */
+int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+            int64_t lda, const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype,
+            void *stream);
+
+/* Same as dg_gemm, but runs kernel `kernel` (an index into the library's
+ * kernel table, see dg_kernel_count / dg_kernel_name) instead of the one the
+ * library would pick; DG_KERNEL_AUTO behaves as dg_gemm.  Returns
+ * DG_ERR_UNSUPPORTED (nothing enqueued) when that kernel does not handle the
+ * problem's dtype, transposes or alignment.  For tests and measurement. */
+int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
+                        void *C, int64_t ldc, int dtype, void *stream, int kernel);
+
+/* The kernel dg_gemm would run for these arguments (host logic only, no GPU
+ * call), or a negative status as dg_gemm would return it. */
+int dg_select_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+                     int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
+                     int dtype);
+
+/* Number of kernels in the table, and a static name for kernel i (NULL when
+ * i is out of range).  Names read "<dtype>_<tiles>_<variant>". */
+int dg_kernel_count(void);
+const char *dg_kernel_name(int kernel);
+
+/* Output tile (rows x cols of C per workgroup) of kernel i; -1 if out of range. */
+int dg_kernel_tile_m(int kernel);
+int dg_kernel_tile_n(int kernel);
+
+/* Static text for a status code. */
+const char *dg_status_string(int status);
+
+/* hipError_t of the calling thread's last DG_ERR_HIP (0 if none). */
+int dg_last_hip_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_H */

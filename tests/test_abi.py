@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the public
+header declares, and its host logic (argument validation, quick returns,
+kernel table and selection) behaves as documented.  No call here reaches a
+GPU: invalid calls and empty problems return before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dense_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    assert "dg_gemm" in names and "dg_status_string" in names and "dg_last_hip_error" in names
+    assert sorted(names) == sorted(dg.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_nm_lists_symbols_as_global_text():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in syms, name
+
+
+NULL = None
+GOOD = dict(ta=0, tb=0, M=16, N=16, K=16, alpha=1.0, A=0x1000, lda=16, B=0x2000, ldb=16, beta=0.0,
+            C=0x3000, ldc=16, dtype=0, stream=NULL)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return dg.dg_gemm(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"],
+                      a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ta=2), -1), (dict(ta=-1), -1), (dict(tb=7), -2),
+    (dict(M=-1), -3), (dict(N=-5), -4), (dict(K=-1), -5), (dict(M=2 ** 31), -3),
+    (dict(A=NULL), -7), (dict(lda=15), -8), (dict(ta=1, lda=15), -8),
+    (dict(B=NULL), -9), (dict(ldb=15), -10), (dict(tb=1, ldb=15), -10),
+    (dict(C=NULL), -12), (dict(ldc=15), -13), (dict(dtype=2), -14), (dict(dtype=-1), -14),
+    # the first invalid argument is the one reported
+    (dict(ta=9, M=-1, dtype=5), -1), (dict(lda=1, ldc=1), -8),
+])
+def test_invalid_arguments(kw, code):
+    assert call(**kw) == code
+    assert dg.dg_status_string(code).startswith("invalid")
+
+
+def test_ld_minimums_follow_the_stored_shape():
+    # A transposed is stored K x M: lda >= M, not K
+    assert call(ta=1, M=32, K=8, lda=8, C=0x3000, ldc=16) == -8
+    assert call(tb=1, N=8, K=32, lda=32, ldb=16, ldc=16) == -10   # B stored N x K: ldb >= K
+    # minimum of 1 on empty extents
+    assert call(M=0, lda=0) == -8
+
+
+def test_empty_problems_return_ok_without_gpu():
+    assert call(M=0) == 0
+    assert call(N=0) == 0
+    assert call(M=0, N=0, A=NULL, B=NULL, C=NULL) == 0
+
+
+def test_null_A_B_allowed_when_not_read():
+    # alpha == 0 or K == 0: A and B are never read, so NULL is accepted by the
+    # checks (the call then only scales C, which needs a GPU: not made here)
+    assert dg.dg_select_kernel(0, 0, 16, 16, 0, NULL, 1, NULL, 16, NULL, 16, 0) >= 0
+
+
+def test_kernel_table():
+    n = dg.dg_kernel_count()
+    names = dg.kernel_names()
+    assert n == len(names) >= 4
+    assert len(set(names)) == n
+    for i, name in enumerate(names):
+        assert name.split("_")[0] in ("f32", "f16")
+        bm, bn = dg.dg_kernel_tile_m(i), dg.dg_kernel_tile_n(i)
+        assert f"{bm}x{bn}" in name
+    assert dg.dg_kernel_name(n) is None and dg.dg_kernel_name(-1) is None
+    assert dg.dg_kernel_tile_m(n) == -1
+
+
+def test_forced_kernel_out_of_range_is_unsupported():
+    a = dict(GOOD)
+    rc = dg.dg_gemm_with_kernel(0, 0, 16, 16, 16, 1.0, 0x1000, 16, 0x2000, 16, 0.0, 0x3000, 16, 0,
+                                NULL, dg.dg_kernel_count())
+    assert rc == dg.DG_ERR_UNSUPPORTED
+    del a
+
+
+def test_selection_picks_matrix_core_kernels_of_the_right_type():
+    for dtype, prefix in ((0, "f32_"), (1, "f16_")):
+        for M, N, K in ((4096, 4096, 4096), (2048, 2048, 2048), (512, 32, 5632), (1, 1, 1),
+                        (8192, 256, 8192), (4095, 4097, 1031)):
+            k = dg.dg_select_kernel(0, 0, M, N, K, NULL, K, NULL, N, NULL, N, dtype)
+            name = dg.dg_kernel_name(k)
+            assert name.startswith(prefix) and "mfma" in name, (M, N, K, name)
+    # the headline shapes get the large tiles
+    k = dg.dg_select_kernel(0, 0, 4096, 4096, 4096, NULL, 4096, NULL, 4096, NULL, 4096, 0)
+    assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 128)
+
+
+def test_tile_grid_matches_the_pages_decompositions():
+    """Output tiles of side T cover C[35,93] at ((35//T)*T, (93//T)*T): the
+    8x8 tile at (32,88) entry (3,5) and the 64x64 tile at (0,64) of the pages
+    (golden file), and for this library's tiles the same arithmetic."""
+    from test_oracle import read_golden
+    g = read_golden("c35_93.txt")
+    r, c = g["row"], g["col"]
+    for t, r0, c0 in ((g["k5_tile"], g["k5_tile_row0"], g["k5_tile_col0"]),
+                      (g["k8_tile"], g["k8_tile_row0"], g["k8_tile_col0"])):
+        assert (r // t * t, c // t * t) == (r0, c0)
+    for i in range(dg.dg_kernel_count()):
+        bm, bn = dg.dg_kernel_tile_m(i), dg.dg_kernel_tile_n(i)
+        assert 0 <= r - (r // bm) * bm < bm and 0 <= c - (c // bn) * bn < bn
+
+
+def test_status_strings():
+    assert dg.dg_status_string(0) == "ok"
+    assert "HIP" in dg.dg_status_string(dg.DG_ERR_HIP)
+    assert dg.dg_status_string(12345) == "unknown status"
+    assert dg.dg_last_hip_error() == 0
+    assert dg.dg_version() >= 100

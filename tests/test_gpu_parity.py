@@ -1,0 +1,239 @@
+"""Parity of the HIP library with the CPU oracle, on an MI355X.
+
+Every case calls the library through its C ABI (dg_gemm / dg_gemm_with_kernel)
+and compares element by element with the oracle within the stated bound:
+|C - ref| <= rtol * (|alpha| sum_k |a_ik b_kj| + |beta C0|) + atol
+(rtol, atol = 2e-5, 1e-6 for fp32; 2e-3, 1e-4 plus half an fp16 ulp for
+fp16), exactly for integer-valued inputs."""
+import functools
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import Problem, check_full, check_sampled
+
+pytestmark = pytest.mark.gpu
+TRANS = list(itertools.product([False, True], [False, True]))
+
+
+@pytest.fixture(scope="module")
+def dg():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_gemm_amd
+    return dense_gemm_amd
+
+
+def kernels_for(dg, dtype):
+    prefix = "f32_" if dtype == "f32" else "f16_"
+    return [i for i, n in enumerate(dg.kernel_names()) if n.startswith(prefix)]
+
+
+# ---------------------------------------------------------------------------
+# every kernel x transpose pair x alignment, ragged shapes over several tiles
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("ta,tb", TRANS)
+@pytest.mark.parametrize("aligned", [True, False])
+def test_every_kernel_ragged(dg, dtype, ta, tb, aligned):
+    if aligned:
+        # every row start 16-byte aligned; edges still cut through 16-byte vectors
+        M, N, K = 311, 263, 197
+        pad = tuple((-x) % 8 + 8 for x in ((M if ta else K), (K if tb else N), N))
+    else:
+        M, N, K = 300, 270, 200   # row strides not a multiple of 16 bytes
+        pad = (3, 5, 1)
+    a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 100 + 2 * ta + tb, with_c0=True)
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype, pad)
+    for k in kernels_for(dg, dtype):
+        print(f"kernel {dg.dg_kernel_name(k)} {dtype} ta={ta} tb={tb} aligned={aligned}", flush=True)
+        check_full(p, kernel=k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_unaligned_pointers(dg, dtype):
+    M, N, K = 129, 257, 77
+    a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 120, with_c0=True)
+    for ta, tb in TRANS:
+        p = Problem(a, b, c0, ta, tb, 1.0, 1.0, dtype, (8, 8, 8))
+        for k in kernels_for(dg, dtype):
+            check_full(p, kernel=k, offset=(1, 3, 1))
+
+
+# ---------------------------------------------------------------------------
+# brute force over every tiny shape
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_all_tiny_shapes(dg, dtype):
+    for M, N, K in itertools.product(range(1, 9), repeat=3):
+        a, b, c0 = synth.problem(M, N, K, dtype, "uniform", M * 100 + N * 10 + K, with_c0=True)
+        ta, tb = TRANS[(M * 7 + N * 3 + K) % 4]
+        alpha, beta = (1.0, 0.0) if (M + N + K) % 2 else (-2.0, 0.5)
+        check_full(Problem(a, b, c0, ta, tb, alpha, beta, dtype, (1, 2, 3)))
+
+
+# ---------------------------------------------------------------------------
+# exact results: integer-valued inputs make every partial sum exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_integer_inputs_exact_and_variants_agree(dg, dtype):
+    M, N, K = 259, 131, 515 if dtype == "f32" else 120   # |sums| stay exact in fp16 output
+    a, b, c0 = synth.problem(M, N, K, dtype, "int2", 130, with_c0=True)
+    exact = a.astype(np.int64) @ b.astype(np.int64) * 2 - c0.astype(np.int64)
+    outs = []
+    for ta, tb in TRANS:
+        for k in kernels_for(dg, dtype):
+            p = Problem(a, b, c0, ta, tb, 2.0, -1.0, dtype, (8, 8, 8))
+            out = p.run_gpu(kernel=k)[:, :N].astype(np.float64)
+            assert np.array_equal(out, exact.astype(np.float64)), (dg.dg_kernel_name(k), ta, tb)
+            outs.append(out)
+
+
+def test_f16_output_rounding_is_rne_and_overflows_to_inf(dg):
+    # integer products summed exactly in fp32, then one RNE rounding to fp16:
+    # the result must equal numpy's RNE conversion of the exact value
+    M, N, K = 64, 96, 256
+    st = synth.Stream(140)
+    a = st.integers((M, K), 0, 16).astype(np.float16)
+    b = st.integers((K, N), 0, 16).astype(np.float16)
+    exact = a.astype(np.int64) @ b.astype(np.int64)          # ~16000 (> 2048: rounds)
+    for alpha in (1.0, 8.0):                                  # 8x: past 65520, -> +inf
+        for ta, tb in TRANS:
+            p = Problem(a, b, None, ta, tb, alpha, 0.0, "f16", (8, 8, 8))
+            out = p.run_gpu()[:, :N]
+            with np.errstate(over="ignore"):
+                want = (alpha * exact.astype(np.float64)).astype(np.float16)
+            assert np.array_equal(out.view(np.uint16), want.view(np.uint16)), (alpha, ta, tb)
+        if alpha == 8.0:
+            assert np.isinf(want).any() and np.isfinite(want).any()
+
+
+# ---------------------------------------------------------------------------
+# alpha / beta / empty cases and what the library does not touch
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_beta_zero_ignores_nan_in_C(dg, dtype):
+    a, b, _ = synth.problem(70, 90, 33, dtype, "uniform", 150)
+    p = Problem(a, b, None, False, True, 1.0, 0.0, dtype, (4, 4, 4))  # C holds NaN
+    check_full(p)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_alpha_zero_and_k_zero_scale_C(dg, dtype):
+    a, b, c0 = synth.problem(50, 60, 20, dtype, "uniform", 151, with_c0=True)
+    a_nan = np.full_like(a, np.nan)
+    p = Problem(a_nan, b, c0, False, False, 0.0, -0.5, dtype, (0, 0, 2))
+    out = p.run_gpu()[:, :60].astype(np.float64)
+    want = (np.float32(-0.5) * c0.astype(np.float32)).astype(a.dtype).astype(np.float64)
+    assert np.array_equal(out, want)
+    p0 = Problem(np.zeros((50, 0), a.dtype), np.zeros((0, 60), a.dtype), c0, False, False, 1.0,
+                 2.0, dtype, (1, 0, 2))
+    out = p0.run_gpu()[:, :60].astype(np.float64)
+    assert np.array_equal(out, (2 * c0.astype(np.float64)))
+    pz = Problem(np.zeros((50, 0), a.dtype), np.zeros((0, 60), a.dtype), None, False, False, 1.0,
+                 0.0, dtype, (1, 0, 2))
+    out = pz.run_gpu()[:, :60].astype(np.float64)
+    assert np.array_equal(out, np.zeros((50, 60)))
+
+
+def test_empty_and_invalid_calls_enqueue_nothing(dg):
+    import torch
+    dev = torch.device("cuda:0")
+    C = torch.full((16, 16), 7.0, device=dev)
+    A = torch.ones((16, 16), device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    ptr = C.data_ptr()
+    # M = 0 and N = 0: nothing to do
+    assert dg.dg_gemm(0, 0, 0, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s) == 0
+    assert dg.dg_gemm(0, 0, 16, 0, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s) == 0
+    # invalid arguments: -i, the 1-based position of the first bad argument
+    bad = [
+        ((2, 0, 16, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s), -1),
+        ((0, 5, 16, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s), -2),
+        ((0, 0, -1, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s), -3),
+        ((0, 0, 16, -1, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s), -4),
+        ((0, 0, 16, 16, -2, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s), -5),
+        ((0, 0, 16, 16, 16, 1.0, None, 16, A.data_ptr(), 16, 0.0, ptr, 16, 0, s), -7),
+        ((0, 0, 16, 16, 16, 1.0, A.data_ptr(), 15, A.data_ptr(), 16, 0.0, ptr, 16, 0, s), -8),
+        ((0, 0, 16, 16, 16, 1.0, A.data_ptr(), 16, None, 16, 0.0, ptr, 16, 0, s), -9),
+        ((0, 0, 16, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 8, 0.0, ptr, 16, 0, s), -10),
+        ((0, 0, 16, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, None, 16, 0, s), -12),
+        ((0, 0, 16, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 15, 0, s), -13),
+        ((0, 0, 16, 16, 16, 1.0, A.data_ptr(), 16, A.data_ptr(), 16, 0.0, ptr, 16, 9, s), -14),
+    ]
+    for args, want in bad:
+        assert dg.dg_gemm(*args) == want, (args, want)
+    torch.cuda.synchronize()
+    assert (C == 7.0).all()
+
+
+def test_side_stream_ordering(dg):
+    """The call is asynchronous on the given stream: work queued before it on
+    that stream is seen, and the result is there after the stream syncs."""
+    import torch
+    dev = torch.device("cuda:0")
+    M = N = K = 512
+    a, b, _ = synth.problem(M, N, K, "f32", "int2", 160)
+    s = torch.cuda.Stream(device=dev)
+    At = torch.from_numpy(a).to(dev)
+    Bt = torch.from_numpy(b).to(dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        Bt.mul_(2.0)                     # queued on s before the GEMM
+        C = dg.gemm(At, Bt)              # runs on s (the current stream)
+    s.synchronize()
+    want = (a.astype(np.int64) @ (2 * b.astype(np.int64))).astype(np.float32)
+    assert np.array_equal(C.cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------------------
+# the measured workloads at their full sizes (sampled elements)
+# ---------------------------------------------------------------------------
+def test_sgemm_512_full(dg):
+    a, b, _ = synth.problem(512, 512, 512, "f32", "uniform", 0)
+    p = Problem(a, b, None, False, False, 1.0, 0.0, "f32")
+    check_full(p)
+
+
+def test_sgemm_4096_nn_sampled(dg):
+    a, b, _ = synth.problem(4096, 4096, 4096, "f32", "uniform", 1)
+    p = Problem(a, b, None, False, False, 1.0, 0.0, "f32")
+    check_sampled(p, n=3000, seed=1)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True)])
+def test_hgemm_2048_sampled(dg, ta, tb):
+    a, b, _ = synth.problem(2048, 2048, 2048, "f16", "normal_sqrtk", 2)
+    p = Problem(a, b, None, ta, tb, 1.0, 0.0, "f16")
+    check_sampled(p, n=3000, seed=2)
+
+
+@pytest.mark.parametrize("index", range(len(synth.LORA_GEMMS)))
+def test_lora_step_gemm(dg, index):
+    name, M, N, K, ta, tb, beta, _ = synth.LORA_GEMMS[index]
+    a, b, c0 = synth.lora_problem(index, seed=3)
+    p = Problem(a, b, c0, ta, tb, 1.0, beta, "f16")
+    print(f"LoRA GEMM {name} ({M}x{N}x{K})", flush=True)
+    if M * N * K <= 64 * 1024 * 1024:
+        check_full(p)
+    else:
+        check_sampled(p, n=2000, seed=index)
+
+
+@functools.lru_cache(maxsize=1)
+def ragged_problem(shape):
+    M, N, K = shape
+    return synth.problem(M, N, K, "f32", "uniform", 4, with_c0=True)
+
+
+@pytest.mark.parametrize("shape", [(4095, 4097, 1031), (8192, 256, 8192)])
+@pytest.mark.parametrize("ta,tb", TRANS)
+def test_sgemm_ragged_full_form(dg, shape, ta, tb):
+    a, b, c0 = ragged_problem(shape)
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, "f32", (8, 8, 8))
+    print(f"ragged {shape} ta={ta} tb={tb}", flush=True)
+    check_sampled(p, n=2000, seed=5)
