@@ -24,6 +24,13 @@ DG_KERNEL_AUTO = -1
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m dense_gemm_amd.build`")
 
+# torch (the owner of the device memory and streams handed to the library)
+# ships its own HIP runtime.  Load it first so the library's libamdhip64.so.7
+# dependency resolves to that same runtime: a second HIP/HSA runtime in the
+# process would not see the device (hipErrorNoDevice), and torch's stream
+# handles are only meaningful to the runtime that created them.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _f32, _vp, _ci = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
 _GEMM_ARGS = [_ci, _ci, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _ci, _vp]
@@ -53,11 +60,23 @@ EXPORTED = ["dg_gemm", "dg_gemm_with_kernel", "dg_select_kernel", "dg_kernel_cou
             "dg_last_hip_error", "dg_version"]
 
 
+def hip_error_name(code: int) -> str:
+    """Name of a hipError_t, from the HIP runtime the library is linked to."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipGetErrorName.restype = ctypes.c_char_p
+        hip.hipGetErrorName.argtypes = [ctypes.c_int]
+        return hip.hipGetErrorName(int(code)).decode()
+    except OSError:
+        return "?"
+
+
 class GemmError(RuntimeError):
     def __init__(self, status: int):
         msg = dg_status_string(status)
         if status == DG_ERR_HIP:
-            msg += f" (hipError_t {dg_last_hip_error()})"
+            e = dg_last_hip_error()
+            msg += f" (hipError_t {e} {hip_error_name(e)})"
         super().__init__(f"dg_gemm failed: {status} ({msg})")
         self.status = status
 

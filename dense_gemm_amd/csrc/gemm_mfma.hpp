@@ -316,9 +316,10 @@ template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, 
 hipError_t launch_mfma(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
-    hipLaunchKernelGGL((gemm_mfma_kernel<T, BM, BN, BK, WM, WN, TA, TB, VEC, MINW>), dim3(nwg),
-                       dim3(256), 0, s, p);
-    return hipGetLastError();
+    GemmParams arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel((const void *)&gemm_mfma_kernel<T, BM, BN, BK, WM, WN, TA, TB, VEC, MINW>,
+                           dim3(nwg), dim3(256), args, 0, s);
 }
 
 }  // namespace dg

@@ -119,8 +119,9 @@ template <typename T, bool TA, bool TB>
 hipError_t launch_simple(const GemmParams &p, hipStream_t s)
 {
     dim3 grid((p.N + ST - 1) / ST, (p.M + ST - 1) / ST);
-    hipLaunchKernelGGL((gemm_simple_kernel<T, TA, TB>), grid, dim3(256), 0, s, p);
-    return hipGetLastError();
+    GemmParams arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel((const void *)&gemm_simple_kernel<T, TA, TB>, grid, dim3(256), args, 0, s);
 }
 
 template <typename T>
@@ -129,8 +130,10 @@ hipError_t launch_scale(const GemmParams &p, hipStream_t s)
     const int64_t total = (int64_t)p.M * p.N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL((scale_c_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, p);
-    return hipGetLastError();
+    GemmParams arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel((const void *)&scale_c_kernel<T>, dim3((unsigned)blocks), dim3(256), args,
+                           0, s);
 }
 
 }  // namespace

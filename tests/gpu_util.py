@@ -65,7 +65,8 @@ class Problem:
                                     At.data_ptr() + oa * es, self.lda, Bt.data_ptr() + ob * es,
                                     self.ldb, self.beta, Ct.data_ptr() + oc * es, self.ldc,
                                     DTYPES[self.dtype], s.cuda_stream, kernel)
-        assert rc == 0, f"dg_gemm returned {rc}: {dg.dg_status_string(rc)}"
+        if rc != 0:
+            raise dg.GemmError(rc)
         s.synchronize()
         out = Ct[oc:oc + self.C0.size].cpu().numpy().reshape(self.C0.shape)
         # nothing outside the buffer view is touched
