@@ -35,6 +35,31 @@ def tflops(M, N, K, seconds):
     return 2.0 * M * N * K / seconds / 1e12
 
 
+def measured_traffic(dtype, kernel, ta, tb, vec=True):
+    """HBM bytes per dispatch of this kernel from the committed counter summary
+    (profiles/hbm_traffic.txt), or None when that summary was taken from other
+    kernel sources than the ones built now."""
+    import hashlib
+    import glob
+    import dense_gemm_amd as dg
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dense_gemm_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    table = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            table[k.strip()] = v.strip()
+    if table.get("sources") != h.hexdigest()[:16]:
+        return None
+    key = (f"{dtype} {dg.dg_kernel_tile_m(kernel)}x{dg.dg_kernel_tile_n(kernel)} "
+           f"{'t' if ta else 'n'}{'t' if tb else 'n'} {'vec' if vec else 'novec'}")
+    return int(float(table[key])) if key in table else None
+
+
 def time_launches(fn, stream, reps):
     """Mean duration of one launch (s), from events on `stream` around reps launches."""
     import torch
@@ -57,6 +82,9 @@ def main():
     ap.add_argument("--no-f16", action="store_true", help="skip the fp16 2048^3 measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 256 MiB device-to-device copy (a kernel of known traffic, "
+                         "to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -73,6 +101,14 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
+
+    if args.copy_calibration:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- fp32 4096^3 nn ---------------------------------------------------
     M = N = K = 4096
@@ -116,7 +152,8 @@ def main():
         "config": {"workload": "SGEMM fp32 row-major nn M=N=K=4096 alpha=1 beta=0",
                    "M": M, "N": N, "K": K, "kernel": dg.dg_kernel_name(kernel)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32, 4),
+                     "traffic": measured_traffic("f32", kernel, 0, 0),
                      "algorithmic_bytes": 3 * M * N * 4, "kernel_ms": round(launch_s * 1e3, 4)},
     }
 
