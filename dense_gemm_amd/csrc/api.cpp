@@ -13,6 +13,7 @@ launch_fn simple_launcher(int dtype, int ta, int tb);
 launch_fn scale_launcher(int dtype);
 const launch_fn *f32_launchers(int config);
 const launch_fn *f16_launchers(int config);
+const launch_fn *f16_pipe_launchers(int config);
 }  // namespace dg
 
 namespace {
@@ -22,28 +23,39 @@ using dg::launch_fn;
 
 thread_local int g_last_hip_error = 0;
 
-// One entry per compiled kernel family.  Matrix-core families come in 8
-// variants: transA x transB x (16-byte vector loads or element loads).
+// One entry per compiled kernel family.
+//   SIMPLE: generic fallback, any problem.
+//   MFMA:   register-staged matrix-core kernels, any shape; 8 variants:
+//           transA x transB x (16-byte vector loads or element loads).
+//   PIPE:   fp16 direct-to-LDS pipelined kernels; 4 variants (transA x transB);
+//           need K % 64 == 0, 16-byte aligned A/B with lda, ldb % 8 == 0, and
+//           the m/n-contiguous operand's extent % 8 == 0.
+enum Kind { SIMPLE, MFMA, PIPE };
 struct Family {
     const char *name;
     int dtype;
     int bm, bn;
     int group_m;
-    bool mfma;
-    const launch_fn *(*variants)(int);  // mfma: table(config)[vec ? 0 : 4 + ta*2 + tb]
+    Kind kind;
+    const launch_fn *(*variants)(int);
     int config;
 };
 
 const Family kFamilies[] = {
-    {"f32_64x64_simple", DG_F32, 64, 64, 1, false, nullptr, 0},
-    {"f16_64x64_simple", DG_F16_F32ACC, 64, 64, 1, false, nullptr, 0},
-    {"f32_256x128_mfma32x32x2", DG_F32, 256, 128, 8, true, dg::f32_launchers, 0},
-    {"f32_128x128_mfma32x32x2", DG_F32, 128, 128, 8, true, dg::f32_launchers, 1},
-    {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, true, dg::f16_launchers, 0},
-    {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, true, dg::f16_launchers, 1},
+    {"f32_64x64_simple", DG_F32, 64, 64, 1, SIMPLE, nullptr, 0},
+    {"f16_64x64_simple", DG_F16_F32ACC, 64, 64, 1, SIMPLE, nullptr, 0},
+    {"f32_256x128_mfma32x32x2", DG_F32, 256, 128, 8, MFMA, dg::f32_launchers, 0},
+    {"f32_128x128_mfma32x32x2", DG_F32, 128, 128, 8, MFMA, dg::f32_launchers, 1},
+    {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, MFMA, dg::f16_launchers, 0},
+    {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, MFMA, dg::f16_launchers, 1},
+    {"f16_128x128_pipe4_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0},
+    {"f16_256x128_pipe3_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
-enum { K_F32_SIMPLE = 0, K_F16_SIMPLE = 1, K_F32_256 = 2, K_F32_128 = 3, K_F16_128 = 4, K_F16_256 = 5 };
+enum {
+    K_F32_SIMPLE = 0, K_F16_SIMPLE = 1, K_F32_256 = 2, K_F32_128 = 3, K_F16_128 = 4, K_F16_256 = 5,
+    K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7
+};
 
 constexpr int64_t kMaxDim = 0x7fffffff;
 
@@ -83,24 +95,33 @@ bool vec_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Kernel choice by dtype and output tile count.  Larger tiles re-read less
-// of A and B; smaller tiles fill more of the 256 compute units.
-int choose(int64_t M, int64_t N, int dtype)
+// Preconditions of the pipelined fp16 kernels (see Family).
+bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+             const void *B, int64_t ldb)
 {
-    if (dtype == DG_F32) {
-        const int64_t big = ceil_div(M, 256) * ceil_div(N, 128);
-        return big >= 384 ? K_F32_256 : K_F32_128;
-    }
+    return K % 64 == 0 && vec_ok(A, lda, B, ldb, DG_F16_F32ACC) && (!ta || M % 8 == 0) &&
+           (tb || N % 8 == 0);
+}
+
+// Kernel choice by dtype, preconditions and output tile count.  Larger tiles
+// re-read less of A and B; smaller tiles fill more of the 256 compute units.
+int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+           const void *B, int64_t ldb, int dtype)
+{
     const int64_t big = ceil_div(M, 256) * ceil_div(N, 128);
+    if (dtype == DG_F32) return big >= 384 ? K_F32_256 : K_F32_128;
+    if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb)) return big >= 512 ? K_F16_PIPE_256 : K_F16_PIPE_128;
     return big >= 512 ? K_F16_256 : K_F16_128;
 }
 
-bool supports(int kernel, int dtype, int64_t M, int64_t N)
+bool supports(int kernel, int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A,
+              int64_t lda, const void *B, int64_t ldb, int dtype)
 {
     if (kernel < 0 || kernel >= kNumKernels) return false;
     const Family &f = kFamilies[kernel];
     if (f.dtype != dtype) return false;
-    if (!f.mfma) return ceil_div(M, 64) <= 65535 && ceil_div(N, 64) <= 0x7fffffff;
+    if (f.kind == SIMPLE) return ceil_div(M, 64) <= 65535;
+    if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb)) return false;
     return ceil_div(M, f.bm) * ceil_div(N, f.bn) <= 0x7fffffff;
 }
 
@@ -135,16 +156,16 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     if (K == 0 || alpha == 0.f) {
         err = dg::scale_launcher(di)(p, s);
     } else {
-        if (kernel == DG_KERNEL_AUTO) kernel = choose(M, N, dtype);
-        if (!supports(kernel, dtype, M, N)) return DG_ERR_UNSUPPORTED;
+        if (kernel == DG_KERNEL_AUTO) kernel = choose(ta, tb, M, N, K, A, lda, B, ldb, dtype);
+        if (!supports(kernel, ta, tb, M, N, K, A, lda, B, ldb, dtype)) return DG_ERR_UNSUPPORTED;
         const Family &f = kFamilies[kernel];
-        if (!f.mfma) {
+        if (f.kind == SIMPLE) {
             err = dg::simple_launcher(di, ta, tb)(p, s);
         } else {
             p.tiles_m = (int32_t)ceil_div(M, f.bm);
             p.tiles_n = (int32_t)ceil_div(N, f.bn);
             p.group_m = f.group_m;
-            const int v = vec_ok(A, lda, B, ldb, dtype) ? 0 : 4;
+            const int v = (f.kind == PIPE || vec_ok(A, lda, B, ldb, dtype)) ? 0 : 4;
             err = f.variants(f.config)[v + ta * 2 + tb](p, s);
         }
     }
@@ -181,7 +202,7 @@ int dg_select_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, co
 {
     int rc = validate(transA, transB, M, N, K, 1.f, A, lda, B, ldb, C, ldc, dtype, false);
     if (rc) return rc;
-    return choose(M, N, dtype);
+    return choose(transA, transB, M, N, K, A, lda, B, ldb, dtype);
 }
 
 int dg_kernel_count(void) { return kNumKernels; }

@@ -1,4 +1,5 @@
 // fp16-operand, fp32-accumulate kernel instantiations (v_mfma_f32_32x32x16_f16).
+#include "gemm_f16_pipe.hpp"
 #include "gemm_mfma.hpp"
 
 namespace dg {
@@ -21,6 +22,18 @@ const launch_fn *f16_launchers(int config)
     static const launch_fn table[2][8] = {
         DG_VARIANTS(_Float16, 128, 128, 64, 64, 64, 1),
         DG_VARIANTS(_Float16, 256, 128, 64, 128, 64, 1),
+    };
+    return table[config];
+}
+
+// pipelined direct-to-LDS kernels: [config][transA * 2 + transB]
+const launch_fn *f16_pipe_launchers(int config)
+{
+    static const launch_fn table[2][4] = {
+        {launch_f16_pipe<128, 128, 64, 64, false, false, 4>, launch_f16_pipe<128, 128, 64, 64, false, true, 4>,
+         launch_f16_pipe<128, 128, 64, 64, true, false, 4>, launch_f16_pipe<128, 128, 64, 64, true, true, 4>},
+        {launch_f16_pipe<256, 128, 128, 64, false, false, 3>, launch_f16_pipe<256, 128, 128, 64, false, true, 3>,
+         launch_f16_pipe<256, 128, 128, 64, true, false, 3>, launch_f16_pipe<256, 128, 128, 64, true, true, 3>},
     };
     return table[config];
 }

@@ -1,0 +1,258 @@
+// fp16-operand / fp32-accumulate GEMM for gfx950 with a multi-stage LDS ring
+// fed by direct global->LDS loads.
+//
+//   C[BM x BN tile] = alpha * sum_k op(A)[rows, k] op(B)[k, cols] + beta * C,
+//   v_mfma_f32_32x32x16_f16 with fp32 accumulators ("Metal GEMM Kernels for
+//   LoRA Training on Apple Silicon", section 1: the fp32 accumulator keeps the
+//   fast path).
+//
+// Why a different kernel from gemm_mfma.hpp: at 2048^3 one 128 x 128 tile per
+// compute unit leaves a single wave per SIMD, and one 64-wide K slab is only
+// ~512 MFMA cycles, shorter than a load round trip.  So the slabs are
+// prefetched STAGES-1 deep, and the loads go straight to LDS
+// (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane),
+// which costs no registers and no transposing VALU work.
+//
+// LDS layouts (both conflict-free for the fragment reads):
+//   k-contiguous operand (A not transposed, B transposed): [BMN][64] halfs,
+//     128-byte rows; the 16-byte chunk c of row r sits at chunk c ^ ((r>>1)&7),
+//     so the 16 rows read together by a quarter wave hit 16 distinct bank
+//     groups.  Fragments: one ds_read_b128 = 8 consecutive k of one row.
+//   m/n-contiguous operand (A transposed, B not transposed): [64][BMN]
+//     halfs, rows of BMN*2 bytes; the 64-byte quad q of row k sits at quad
+//     q ^ (k&3).  Fragments come from ds_read_b64_tr_b16, the hardware
+//     transposing read: in each 16-lane group, lanes 4t..4t+3 name row t of a
+//     4 x 16 block and lane j receives column j, i.e. 4 consecutive k of its
+//     own m (or n) -- the MFMA operand layout -- with no write-side transpose
+//     (the page's section 3 transposes on the write; gfx950 can do it on the
+//     read).
+// The swizzle is applied by choosing which global address each lane fetches,
+// since a direct load writes its lanes contiguously.
+//
+// Pipeline per K slab kt (one barrier per slab):
+//   wait for this thread's loads of slab kt; barrier (slab kt visible to all,
+//   and everyone is done reading slab kt-1); issue the loads of slab
+//   kt+STAGES-1 into the stage slab kt-1 used; MFMAs on slab kt.
+//
+// Host-side preconditions (checked by the dispatcher): K % 64 == 0; A and B
+// 16-byte aligned with lda, ldb multiples of 8; the m/n-contiguous operand's
+// extent (M if A is transposed, N if B is not) a multiple of 8.  Rows or
+// columns past M or N are fetched from a clamped, valid address; they only
+// feed outputs that the guarded epilogue never stores.
+#pragma once
+
+#include "gemm_common.hpp"
+
+namespace dg {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+constexpr int PIPE_BK = 64;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One operand of the pipelined kernel.
+//   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
+template <int BMN, bool KCONT>
+struct PipeOperand {
+    static constexpr int BYTES = BMN * PIPE_BK * 2;   // one stage
+    static constexpr int LOADS = BYTES / (256 * 16);  // 16-byte loads per thread per slab
+    static_assert(LOADS * 256 * 16 == BYTES, "slab must split into 16-byte loads");
+    static constexpr int ROW_BYTES = KCONT ? PIPE_BK * 2 : BMN * 2;
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide load fills
+
+    const _Float16 *ptr[LOADS];  // per-lane global addresses of the current slab
+    int64_t step;                // elements to advance per slab
+
+    // Per-lane addresses for the slab at k = 0.  mn0: first row (m or n) of
+    // the tile; ext: M or N; ld: row stride of the stored matrix.
+    __device__ __forceinline__ void init(const _Float16 *g, int64_t ld, int mn0, int ext, int wave,
+                                         int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int rbase = (i * 4 + wave) * ROWS_PER_LOAD;  // first LDS row of this load
+            if constexpr (KCONT) {
+                const int r = rbase + (lane >> 3);
+                const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical 16-byte chunk (8 k)
+                int row = mn0 + r;
+                row = row < ext ? row : ext - 1;
+                ptr[i] = g + (int64_t)row * ld + c * 8;
+            } else {
+                const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
+                const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
+                const int q = (p >> 2) ^ (r & 3);                 // logical 64-byte quad
+                int col = mn0 + q * 32 + (p & 3) * 8;
+                col = col < ext ? col : ext - 8;
+                ptr[i] = g + (int64_t)r * ld + col;
+            }
+        }
+        step = KCONT ? PIPE_BK : PIPE_BK * ld;
+    }
+
+    // Issue this slab's direct loads into the stage at `lds` and advance.
+    // The load is written as inline asm so that the compiler does not track
+    // it: it would otherwise wait for every direct load in flight (all
+    // prefetched slabs) before each LDS read and barrier.  Completion is
+    // instead awaited explicitly with wait_vmcnt (vector-memory loads retire
+    // in order).  M0 holds the wave-uniform LDS destination; each lane's 16
+    // bytes land at M0 + 16 * lane.
+    __device__ __forceinline__ void issue(lds_char_t *lds, int wave)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const unsigned dst = (unsigned)(uintptr_t)(lds + (i * 4 + wave) * 1024);
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                         : "memory");
+            ptr[i] += step;
+        }
+    }
+
+    // MFMA operand of block rows [b0, b0+32) for k-step kk (16 k) of a stage.
+    __device__ __forceinline__ f16x8 frag(const lds_char_t *lds, int b0, int kk, int lane) const
+    {
+        if constexpr (KCONT) {
+            const int r = b0 + (lane & 31);
+            const int c = 2 * kk + (lane >> 5);
+            const int p = c ^ ((r >> 1) & 7);
+            return *(const lds_f16x8_t *)(lds + r * ROW_BYTES + p * 16);
+        } else {
+            const int g = lane >> 4, j = lane & 15, t = j >> 2, s = j & 3;
+            const int q = b0 >> 5;
+            const int colb = (16 * (g & 1) + 4 * s) * 2;   // byte offset inside the 64-byte quad
+            const int k0 = 16 * kk + 8 * (g >> 1) + t;
+            const lds_char_t *p0 = lds + k0 * ROW_BYTES + ((q ^ t) << 6) + colb;
+            const lds_char_t *p1 = p0 + 4 * ROW_BYTES;      // rows k0 + 4 (same k & 3)
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(f16x8, v);
+        }
+    }
+};
+
+template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm_f16_pipe_kernel(GemmParams p)
+{
+    constexpr int WAVES_N = BN / WN;
+    static_assert((BM / WM) * WAVES_N == 4, "4 waves per workgroup");
+    constexpr int TM = WM / 32, TN = WN / 32;
+    typedef PipeOperand<BM, !TA> OpA;
+    typedef PipeOperand<BN, TB> OpB;
+    constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * STAGE_BYTES];
+    lds_char_t *smem = (lds_char_t *)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / WAVES_N) * WM;
+    const int wn0 = (wave % WAVES_N) * WN;
+    int tm, tn;
+    tile_coords(blockIdx.x, p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = p.K / PIPE_BK;
+
+    OpA ga;
+    OpB gb;
+    ga.init((const _Float16 *)p.A, p.lda, m0, p.M, wave, lane);
+    gb.init((const _Float16 *)p.B, p.ldb, n0, p.N, wave, lane);
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+        if (s < nk) {
+            ga.issue(smem + s * STAGE_BYTES, wave);
+            gb.issue(smem + s * STAGE_BYTES + OpA::BYTES, wave);
+        }
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    constexpr int LOADS = OpA::LOADS + OpB::LOADS;
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        // this thread's loads of slab kt are done once at most the loads of
+        // the slabs issued after it are outstanding
+        if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * LOADS>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + STAGES - 1 < nk) {
+            const int ns = (stage == 0 ? STAGES : stage) - 1;   // stage of slab kt-1
+            ga.issue(smem + ns * STAGE_BYTES, wave);
+            gb.issue(smem + ns * STAGE_BYTES + OpA::BYTES, wave);
+        }
+        const lds_char_t *sA = smem + stage * STAGE_BYTES;
+        const lds_char_t *sB = sA + OpA::BYTES;
+#pragma unroll
+        for (int kk = 0; kk < PIPE_BK / 16; ++kk) {
+            f16x8 a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = ga.frag(sA, wm0 + 32 * i, kk, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) b[j] = gb.frag(sB, wn0 + 32 * j, kk, lane);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        stage = (stage + 1 == STAGES) ? 0 : stage + 1;
+    }
+
+    // Epilogue: accumulator register r of lane l in a 32x32 block holds row
+    // 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    _Float16 *C = (_Float16 *)p.C;
+    const int lcol = lane & 31;
+    const int lrow4 = (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn0 + 32 * j + lcol;
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + lrow4 + (r & 3);
+                if (row < p.M) {
+                    _Float16 *c = C + (int64_t)row * p.ldc + col;
+                    float v = p.alpha * acc[i][j][r];
+                    if (p.beta != 0.f) v = __builtin_fmaf(p.beta, (float)*c, v);
+                    *c = (_Float16)v;
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES>
+hipError_t launch_f16_pipe(const GemmParams &p, hipStream_t s)
+{
+    const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+    GemmParams arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel((const void *)&gemm_f16_pipe_kernel<BM, BN, WM, WN, TA, TB, STAGES>,
+                           dim3(nwg), dim3(256), args, 0, s);
+}
+
+}  // namespace dg

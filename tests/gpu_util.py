@@ -82,8 +82,9 @@ class Problem:
         return self.c0 if (self.beta != 0.0 and self.c0 is not None) else None
 
 
-def check_full(p: Problem, kernel=-1, offset=(0, 0, 0)):
-    out = p.run_gpu(kernel, offset)
+def check_full(p: Problem, kernel=-1, offset=(0, 0, 0), out=None):
+    if out is None:
+        out = p.run_gpu(kernel, offset)
     p.check_padding(out)
     got = out[:, :p.N].astype(np.float64)
     ref, ab = p.oracle_full()

@@ -33,6 +33,25 @@ def kernels_for(dg, dtype):
     return [i for i, n in enumerate(dg.kernel_names()) if n.startswith(prefix)]
 
 
+def pipe_ok(p):
+    """Preconditions of the pipelined fp16 kernels (as the header states)."""
+    return (p.K % 64 == 0 and p.lda % 8 == 0 and p.ldb % 8 == 0 and (not p.ta or p.M % 8 == 0)
+            and (p.tb or p.N % 8 == 0))
+
+
+def run_or_unsupported(dg, p, k, **kw):
+    """Runs kernel k; returns None when the library rejects it as unsupported
+    for this problem, which is only allowed for the pipelined kernels when
+    their preconditions fail."""
+    try:
+        return p.run_gpu(kernel=k, **kw)
+    except dg.GemmError as e:
+        assert e.status == dg.DG_ERR_UNSUPPORTED, e
+        assert "pipe" in dg.dg_kernel_name(k) and (not pipe_ok(p) or kw.get("offset")), \
+            f"{dg.dg_kernel_name(k)} rejected a problem it should take"
+        return None
+
+
 # ---------------------------------------------------------------------------
 # every kernel x transpose pair x alignment, ragged shapes over several tiles
 # ---------------------------------------------------------------------------
@@ -51,7 +70,26 @@ def test_every_kernel_ragged(dg, dtype, ta, tb, aligned):
     p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype, pad)
     for k in kernels_for(dg, dtype):
         print(f"kernel {dg.dg_kernel_name(k)} {dtype} ta={ta} tb={tb} aligned={aligned}", flush=True)
-        check_full(p, kernel=k)
+        out = run_or_unsupported(dg, p, k)
+        if out is not None:
+            check_full(p, kernel=k, out=out)
+
+
+@pytest.mark.parametrize("ta,tb", TRANS)
+@pytest.mark.parametrize("shape", [(296, 264, 192), (1000, 1032, 512), (136, 8, 64), (8, 136, 128),
+                                   (264, 520, 256)])
+def test_pipelined_f16_kernels(dg, ta, tb, shape):
+    """The direct-to-LDS pipelined kernels on shapes meeting their
+    preconditions: ragged M and N (clamped loads), one and two K slabs (the
+    pipeline tail), several tiles."""
+    M, N, K = shape
+    a, b, c0 = synth.problem(M, N, K, "f16", "uniform", 170 + 2 * ta + tb, with_c0=True)
+    p = Problem(a, b, c0, ta, tb, 0.75, 0.5, "f16", (8, 8, 8))
+    assert pipe_ok(p)
+    for k in kernels_for(dg, "f16"):
+        if "pipe" in dg.dg_kernel_name(k):
+            print(f"kernel {dg.dg_kernel_name(k)} {shape} ta={ta} tb={tb}", flush=True)
+            check_full(p, kernel=k)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
@@ -61,7 +99,9 @@ def test_unaligned_pointers(dg, dtype):
     for ta, tb in TRANS:
         p = Problem(a, b, c0, ta, tb, 1.0, 1.0, dtype, (8, 8, 8))
         for k in kernels_for(dg, dtype):
-            check_full(p, kernel=k, offset=(1, 3, 1))
+            out = run_or_unsupported(dg, p, k, offset=(1, 3, 1))
+            if out is not None:
+                check_full(p, kernel=k, out=out)
 
 
 # ---------------------------------------------------------------------------
@@ -81,14 +121,17 @@ def test_all_tiny_shapes(dg, dtype):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_integer_inputs_exact_and_variants_agree(dg, dtype):
-    M, N, K = 259, 131, 515 if dtype == "f32" else 120   # |sums| stay exact in fp16 output
+    M, N, K = (259, 131, 515) if dtype == "f32" else (259, 136, 128)  # |sums| exact in fp16
     a, b, c0 = synth.problem(M, N, K, dtype, "int2", 130, with_c0=True)
     exact = a.astype(np.int64) @ b.astype(np.int64) * 2 - c0.astype(np.int64)
     outs = []
     for ta, tb in TRANS:
         for k in kernels_for(dg, dtype):
             p = Problem(a, b, c0, ta, tb, 2.0, -1.0, dtype, (8, 8, 8))
-            out = p.run_gpu(kernel=k)[:, :N].astype(np.float64)
+            out = run_or_unsupported(dg, p, k)
+            if out is None:
+                continue
+            out = out[:, :N].astype(np.float64)
             assert np.array_equal(out, exact.astype(np.float64)), (dg.dg_kernel_name(k), ta, tb)
             outs.append(out)
 
