@@ -48,13 +48,14 @@ const Family kFamilies[] = {
     {"f32_128x128_mfma32x32x2", DG_F32, 128, 128, 8, MFMA, dg::f32_launchers, 1},
     {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, MFMA, dg::f16_launchers, 0},
     {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, MFMA, dg::f16_launchers, 1},
-    {"f16_128x128_pipe4_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0},
-    {"f16_256x128_pipe3_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1},
+    {"f16_128x128_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0},
+    {"f16_256x128_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1},
+    {"f16_128x128_pipe2_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 2},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
     K_F32_SIMPLE = 0, K_F16_SIMPLE = 1, K_F32_256 = 2, K_F32_128 = 3, K_F16_128 = 4, K_F16_256 = 5,
-    K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7
+    K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7, K_F16_PIPE_128_2 = 8
 };
 
 constexpr int64_t kMaxDim = 0x7fffffff;
@@ -110,7 +111,13 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
 {
     const int64_t big = ceil_div(M, 256) * ceil_div(N, 128);
     if (dtype == DG_F32) return big >= 384 ? K_F32_256 : K_F32_128;
-    if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb)) return big >= 512 ? K_F16_PIPE_256 : K_F16_PIPE_128;
+    if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb)) {
+        // enough 256x128 tiles for two per CU: the big tile; enough 128x128
+        // tiles for two per CU: the shallow two-workgroup pipeline; else the
+        // deep one-workgroup pipeline
+        if (big >= 512) return K_F16_PIPE_256;
+        return ceil_div(M, 128) * ceil_div(N, 128) >= 512 ? K_F16_PIPE_128_2 : K_F16_PIPE_128;
+    }
     return big >= 512 ? K_F16_256 : K_F16_128;
 }
 
@@ -149,6 +156,7 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     p.beta = beta;
     p.tiles_m = p.tiles_n = 0;
     p.group_m = 1;
+    p.c_vec = aligned16(C) && ldc % (dtype == DG_F32 ? 4 : 8) == 0;
     hipStream_t s = (hipStream_t)stream;
     const int di = dtype == DG_F32 ? 0 : 1;
 

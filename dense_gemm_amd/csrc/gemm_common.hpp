@@ -21,6 +21,7 @@ struct GemmParams {
     float alpha, beta;
     int32_t tiles_m, tiles_n;  // output tiles of the launch
     int32_t group_m;           // tile rows walked together (cache locality)
+    int32_t c_vec;             // C rows start on 16-byte boundaries (16-byte stores allowed)
 };
 
 // A host-side launcher: enqueues one kernel on `stream`, returns a hipError_t.

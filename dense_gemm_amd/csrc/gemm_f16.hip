@@ -27,13 +27,18 @@ const launch_fn *f16_launchers(int config)
 }
 
 // pipelined direct-to-LDS kernels: [config][transA * 2 + transB]
+//   0: 128x128 tile, 4 stages, two K groups of 4 waves (one workgroup per CU)
+//   1: 256x128 tile, 2 stages, eight 64x64 waves
+//   2: 128x128 tile, 2 stages, two K groups (two workgroups per CU)
 const launch_fn *f16_pipe_launchers(int config)
 {
-    static const launch_fn table[2][4] = {
-        {launch_f16_pipe<128, 128, 64, 64, false, false, 4>, launch_f16_pipe<128, 128, 64, 64, false, true, 4>,
-         launch_f16_pipe<128, 128, 64, 64, true, false, 4>, launch_f16_pipe<128, 128, 64, 64, true, true, 4>},
-        {launch_f16_pipe<256, 128, 128, 64, false, false, 3>, launch_f16_pipe<256, 128, 128, 64, false, true, 3>,
-         launch_f16_pipe<256, 128, 128, 64, true, false, 3>, launch_f16_pipe<256, 128, 128, 64, true, true, 3>},
+    static const launch_fn table[3][4] = {
+        {launch_f16_pipe<128, 128, 64, 64, false, false, 4, 2>, launch_f16_pipe<128, 128, 64, 64, false, true, 4, 2>,
+         launch_f16_pipe<128, 128, 64, 64, true, false, 4, 2>, launch_f16_pipe<128, 128, 64, 64, true, true, 4, 2>},
+        {launch_f16_pipe<256, 128, 64, 64, false, false, 2, 1>, launch_f16_pipe<256, 128, 64, 64, false, true, 2, 1>,
+         launch_f16_pipe<256, 128, 64, 64, true, false, 2, 1>, launch_f16_pipe<256, 128, 64, 64, true, true, 2, 1>},
+        {launch_f16_pipe<128, 128, 64, 64, false, false, 2, 2>, launch_f16_pipe<128, 128, 64, 64, false, true, 2, 2>,
+         launch_f16_pipe<128, 128, 64, 64, true, false, 2, 2>, launch_f16_pipe<128, 128, 64, 64, true, true, 2, 2>},
     };
     return table[config];
 }

@@ -32,7 +32,9 @@
 // Pipeline per K slab kt (one barrier per slab):
 //   wait for this thread's loads of slab kt; barrier (slab kt visible to all,
 //   and everyone is done reading slab kt-1); issue the loads of slab
-//   kt+STAGES-1 into the stage slab kt-1 used; MFMAs on slab kt.
+//   kt+STAGES-1 into the stage slab kt-1 used; MFMAs on slab kt.  (Moving the
+//   barrier into the middle of a slab, to overlap the next slab's first LDS
+//   reads with MFMAs, measured slower: it drains the MFMA queue mid-slab.)
 //
 // Host-side preconditions (checked by the dispatcher): K % 64 == 0; A and B
 // 16-byte aligned with lda, ldb multiples of 8; the m/n-contiguous operand's
@@ -64,11 +66,11 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // One operand of the pipelined kernel.
 //   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
-template <int BMN, bool KCONT>
+template <int BMN, bool KCONT, int NW>
 struct PipeOperand {
-    static constexpr int BYTES = BMN * PIPE_BK * 2;   // one stage
-    static constexpr int LOADS = BYTES / (256 * 16);  // 16-byte loads per thread per slab
-    static_assert(LOADS * 256 * 16 == BYTES, "slab must split into 16-byte loads");
+    static constexpr int BYTES = BMN * PIPE_BK * 2;      // one stage
+    static constexpr int LOADS = BYTES / (NW * 64 * 16);  // 16-byte loads per thread per slab
+    static_assert(LOADS * NW * 64 * 16 == BYTES, "slab must split into 16-byte loads");
     static constexpr int ROW_BYTES = KCONT ? PIPE_BK * 2 : BMN * 2;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide load fills
 
@@ -82,7 +84,7 @@ struct PipeOperand {
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int rbase = (i * 4 + wave) * ROWS_PER_LOAD;  // first LDS row of this load
+            const int rbase = (i * NW + wave) * ROWS_PER_LOAD;  // first LDS row of this load
             if constexpr (KCONT) {
                 const int r = rbase + (lane >> 3);
                 const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical 16-byte chunk (8 k)
@@ -112,7 +114,7 @@ struct PipeOperand {
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const unsigned dst = (unsigned)(uintptr_t)(lds + (i * 4 + wave) * 1024);
+            const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
             asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                          :
                          : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
@@ -145,23 +147,47 @@ struct PipeOperand {
     }
 };
 
-template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES>
-__global__ __launch_bounds__(256, 1) void gemm_f16_pipe_kernel(GemmParams p)
+// Waves: (BM/WM) x (BN/WN) sub-tiles per K group, KSPLIT groups.  Group g
+// runs the 16-k steps [g*4/KSPLIT, (g+1)*4/KSPLIT) of every slab, so with a
+// 128 x 128 tile of 64 x 64 sub-tiles and KSPLIT = 2 each SIMD holds two
+// waves (one per group): while one waits on LDS or the barrier the other
+// keeps the matrix core busy, at unchanged LDS read traffic per MFMA.  At the
+// end the two partial accumulators of a sub-tile are summed through LDS: each
+// wave keeps half of its blocks and hands the other half to its partner (the
+// same sub-tile in the other group).  A 256 x 128 tile gets its two waves per
+// SIMD from eight 64 x 64 sub-tiles instead (KSPLIT = 1).
+template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f16_pipe_kernel(GemmParams p)
 {
     constexpr int WAVES_N = BN / WN;
-    static_assert((BM / WM) * WAVES_N == 4, "4 waves per workgroup");
+    constexpr int NWG = (BM / WM) * WAVES_N;       // waves per K group
+    constexpr int NW = NWG * KSPLIT;               // waves per workgroup
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     constexpr int TM = WM / 32, TN = WN / 32;
-    typedef PipeOperand<BM, !TA> OpA;
-    typedef PipeOperand<BN, TB> OpB;
+    constexpr int NB = TM * TN;                    // 32x32 blocks per wave
+    constexpr int KPW = (PIPE_BK / 16) / KSPLIT;   // 16-k steps per wave per slab
+    static_assert(KPW >= 1 && KPW * KSPLIT == PIPE_BK / 16, "K split");
+    static_assert(KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
+    typedef PipeOperand<BM, !TA, NW> OpA;
+    typedef PipeOperand<BN, TB, NW> OpB;
     constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * STAGE_BYTES];
+    constexpr int SMEM = STAGES * STAGE_BYTES;
+    constexpr int XCHG_BYTES = NW * (NB / 2) * 4096;     // partner exchange
+    constexpr int EPI_LD = 40;                           // floats per staged row (32 + 8)
+    constexpr int EPI_BYTES = NW * 32 * EPI_LD * 4;      // epilogue staging, one block per wave
+    static_assert(KSPLIT == 1 || XCHG_BYTES <= SMEM, "exchange fits the ring");
+    static_assert(EPI_BYTES <= SMEM, "epilogue staging fits the ring");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     lds_char_t *smem = (lds_char_t *)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave / WAVES_N) * WM;
-    const int wn0 = (wave % WAVES_N) * WN;
+    const int kgroup = wave / NWG;
+    const int wq = wave % NWG;
+    const int wm0 = (wq / WAVES_N) * WM;
+    const int wn0 = (wq % WAVES_N) * WN;
+    const int kk0 = kgroup * KPW;
     int tm, tn;
     tile_coords(blockIdx.x, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -190,10 +216,13 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_pipe_kernel(GemmParams p)
                 acc[i][j][r] = 0.f;
 
     constexpr int LOADS = OpA::LOADS + OpB::LOADS;
+    // One barrier per slab, at its start: slab kt is then in LDS for every
+    // wave and every wave is done with slab kt-1, whose stage receives the
+    // loads of slab kt+STAGES-1.  The slab's MFMAs follow, the compiler
+    // interleaving the fragment reads with them; a wave waiting at the next
+    // barrier still has its last MFMAs in flight.
     int stage = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        // this thread's loads of slab kt are done once at most the loads of
-        // the slabs issued after it are outstanding
         if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * LOADS>();
         else wait_vmcnt<0>();
         __syncthreads();
@@ -205,7 +234,8 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_pipe_kernel(GemmParams p)
         const lds_char_t *sA = smem + stage * STAGE_BYTES;
         const lds_char_t *sB = sA + OpA::BYTES;
 #pragma unroll
-        for (int kk = 0; kk < PIPE_BK / 16; ++kk) {
+        for (int s = 0; s < KPW; ++s) {
+            const int kk = kk0 + s;
             f16x8 a[TM], b[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i) a[i] = ga.frag(sA, wm0 + 32 * i, kk, lane);
@@ -220,39 +250,121 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_pipe_kernel(GemmParams p)
         stage = (stage + 1 == STAGES) ? 0 : stage + 1;
     }
 
-    // Epilogue: accumulator register r of lane l in a 32x32 block holds row
-    // 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    // ---- sum the K groups' partial accumulators (KSPLIT == 2) ---------------
+    // Block q (= i*TN + j) belongs to group 0 when q < NB/2, else to group 1.
+    // Each wave writes the blocks it does not own to its exchange slot, in
+    // increasing q, 16 bytes per lane per 4 registers.
+    __syncthreads();  // every wave is done with the ring
+    if constexpr (KSPLIT == 2) {
+        lds_char_t *mine = smem + wave * (NB / 2) * 4096;
+        const lds_char_t *theirs = smem + ((wave + NWG) % NW) * (NB / 2) * 4096;
+        int w = 0;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const bool own = (q < NB / 2) == (kgroup == 0);
+            if (!own) {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const f32x16 &v = acc[q / TN][q % TN];
+                    const f32x4 x = {v[4 * c4], v[4 * c4 + 1], v[4 * c4 + 2], v[4 * c4 + 3]};
+                    *(__attribute__((address_space(3))) f32x4 *)(mine + w * 4096 + c4 * 1024 + lane * 16) = x;
+                }
+                ++w;
+            }
+        }
+        __syncthreads();
+        int rd = 0;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const bool own = (q < NB / 2) == (kgroup == 0);
+            if (own) {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(theirs + rd * 4096 + c4 * 1024 + lane * 16);
+                    f32x16 &v = acc[q / TN][q % TN];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[4 * c4 + e] += x[e];
+                }
+                ++rd;
+            }
+        }
+        __syncthreads();  // exchange slots are reused for the epilogue staging
+    }
+
+    // ---- epilogue --------------------------------------------------------------
+    // Accumulator register r of lane l in a 32x32 block holds row
+    // 8*(r/4) + 4*(l/32) + r%4, column l%32.  Each owned block is staged in
+    // this wave's LDS slot as fp32 [32][EPI_LD]; lane l then takes row l/2,
+    // columns 16*(l%2) .. +15, and writes them with two 16-byte stores (one
+    // rounding to fp16 per element), or element by element at the matrix
+    // edge or when C rows are not 16-byte aligned.
     _Float16 *C = (_Float16 *)p.C;
-    const int lcol = lane & 31;
-    const int lrow4 = (lane >> 5) * 4;
+    lds_char_t *stg = smem + wave * 32 * EPI_LD * 4;
+    typedef __attribute__((address_space(3))) float lds_float_t;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int q = 0; q < NB; ++q) {
+        const bool own = KSPLIT == 1 || ((q < NB / 2) == (kgroup == 0));
+        if (!own) continue;
+        const int i = q / TN, j = q % TN;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn0 + 32 * j + lcol;
-            if (col >= p.N) continue;
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+            *(lds_float_t *)(stg + (row * EPI_LD + (lane & 31)) * 4) = acc[i][j][r];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is staged
+        __builtin_amdgcn_wave_barrier();
+        const int lr = lane >> 1, lc = (lane & 1) * 16;
+        float v[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + lrow4 + (r & 3);
-                if (row < p.M) {
-                    _Float16 *c = C + (int64_t)row * p.ldc + col;
-                    float v = p.alpha * acc[i][j][r];
-                    if (p.beta != 0.f) v = __builtin_fmaf(p.beta, (float)*c, v);
-                    *c = (_Float16)v;
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const f32x4 x = *(const lds_f32x4_t *)(stg + (lr * EPI_LD + lc + 4 * c4) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * c4 + e] = p.alpha * x[e];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the slot is rewritten
+        __builtin_amdgcn_wave_barrier();
+        const int grow = m0 + wm0 + 32 * i + lr;
+        const int gcol = n0 + wn0 + 32 * j + lc;
+        _Float16 *c = C + (int64_t)grow * p.ldc + gcol;
+        if (p.c_vec && grow < p.M && gcol + 16 <= p.N) {
+            if (p.beta != 0.f) {
+                const f16x8 c0 = *(const f16x8 *)c, c1 = *(const f16x8 *)(c + 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[e] = __builtin_fmaf(p.beta, (float)c0[e], v[e]);
+                    v[8 + e] = __builtin_fmaf(p.beta, (float)c1[e], v[8 + e]);
+                }
+            }
+            f16x8 o0, o1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o0[e] = (_Float16)v[e];
+                o1[e] = (_Float16)v[8 + e];
+            }
+            *(f16x8 *)c = o0;
+            *(f16x8 *)(c + 8) = o1;
+        } else if (grow < p.M) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                if (gcol + e < p.N) {
+                    float x = v[e];
+                    if (p.beta != 0.f) x = __builtin_fmaf(p.beta, (float)c[e], x);
+                    c[e] = (_Float16)x;
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES>
+template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
 hipError_t launch_f16_pipe(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_f16_pipe_kernel<BM, BN, WM, WN, TA, TB, STAGES>,
-                           dim3(nwg), dim3(256), args, 0, s);
+    return hipLaunchKernel((const void *)&gemm_f16_pipe_kernel<BM, BN, WM, WN, TA, TB, STAGES, KSPLIT>,
+                           dim3(nwg), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
 }
 
 }  // namespace dg
