@@ -73,6 +73,53 @@ def time_launches(fn, stream, reps):
     return start.elapsed_time(end) / 1e3 / reps
 
 
+def lora_step(dev, stream, reps):
+    """Times the 18 GEMMs of one LoRA MLP-block step (512 tokens, d_model 2048,
+    FFN 5632, rank 32; fp16 operands, fp32 accumulation) back to back on one
+    stream, and each GEMM on its own (events around repeated launches)."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_amd as dg
+    import synth
+
+    sptr = stream.cuda_stream
+    calls = []
+    for idx, (name, M, N, K, ta, tb, beta, _) in enumerate(synth.LORA_GEMMS):
+        a, b, c0 = synth.lora_problem(idx, seed=3)
+        A = torch.from_numpy(np.ascontiguousarray(a.T if ta else a)).to(dev)
+        B = torch.from_numpy(np.ascontiguousarray(b.T if tb else b)).to(dev)
+        C = torch.from_numpy(c0).to(dev) if c0 is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
+        lda, ldb = (M if ta else K), (K if tb else N)
+        k = dg.dg_select_kernel(ta, tb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), N,
+                                dg.DG_F16_F32ACC)
+
+        def f(ta=ta, tb=tb, M=M, N=N, K=K, A=A, B=B, C=C, lda=lda, ldb=ldb, beta=beta):
+            rc = dg.dg_gemm(ta, tb, M, N, K, 1.0, A.data_ptr(), lda, B.data_ptr(), ldb, beta,
+                            C.data_ptr(), N, dg.DG_F16_F32ACC, sptr)
+            if rc != 0:
+                raise dg.GemmError(rc)
+        calls.append((name, M, N, K, f, dg.dg_kernel_name(k)))
+
+    def step():
+        for c in calls:
+            c[4]()
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    t_step = time_launches(step, stream, reps)
+    flops = sum(2.0 * M * N * K for _, M, N, K, _, _ in calls)
+    per = []
+    for name, M, N, K, f, kname in calls:
+        t = time_launches(f, stream, reps)
+        per.append({"gemm": name, "M": M, "N": N, "K": K, "us": round(t * 1e6, 2),
+                    "tflops": round(2.0 * M * N * K / t / 1e12, 2), "kernel": kname})
+    return {"step_ms": round(t_step * 1e3, 4), "gflop": round(flops / 1e9, 3),
+            "tflops": round(flops / t_step / 1e12, 2),
+            "tokens_per_s": round(512 / t_step, 1), "per_gemm": per}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,6 +127,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-f16", action="store_true", help="skip the fp16 2048^3 measurements")
+    ap.add_argument("--no-lora", action="store_true", help="skip the LoRA-step GEMM sequence")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -184,6 +232,10 @@ def main():
             res[name] = {"tflops": round(ach, 2), "frac": round(ach / PEAK_F16, 4),
                          "kernel_us": round(t16 * 1e6, 2), "kernel": dg.dg_kernel_name(k16)}
         out["fp16_2048"] = {"peak": PEAK_F16, "unit": "TFLOP/s", **res}
+
+    # ---- LoRA MLP-block step: the 18 fp16 GEMMs of one forward + backward -------
+    if not args.no_lora:
+        out["lora_step"] = lora_step(dev, stream, max(args.steps, 20))
 
     # ---- CPU baseline: the oracle on whole rows of the same problem -------------
     if not args.no_cpu:

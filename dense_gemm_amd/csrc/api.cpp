@@ -28,8 +28,8 @@ thread_local int g_last_hip_error = 0;
 //   MFMA:   register-staged matrix-core kernels, any shape; 8 variants:
 //           transA x transB x (16-byte vector loads or element loads).
 //   PIPE:   fp16 direct-to-LDS pipelined kernels; 4 variants (transA x transB);
-//           need K % 64 == 0, 16-byte aligned A/B with lda, ldb % 8 == 0, and
-//           the m/n-contiguous operand's extent % 8 == 0.
+//           need 16-byte aligned A/B with lda, ldb % 8 == 0, and the
+//           m/n-contiguous operand's extent % 8 == 0.
 enum Kind { SIMPLE, MFMA, PIPE };
 struct Family {
     const char *name;
@@ -100,8 +100,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
              const void *B, int64_t ldb)
 {
-    return K % 64 == 0 && vec_ok(A, lda, B, ldb, DG_F16_F32ACC) && (!ta || M % 8 == 0) &&
-           (tb || N % 8 == 0);
+    return vec_ok(A, lda, B, ldb, DG_F16_F32ACC) && (!ta || M % 8 == 0) && (tb || N % 8 == 0);
 }
 
 // Kernel choice by dtype, preconditions and output tile count.  Larger tiles

@@ -36,9 +36,10 @@
 //   barrier into the middle of a slab, to overlap the next slab's first LDS
 //   reads with MFMAs, measured slower: it drains the MFMA queue mid-slab.)
 //
-// Host-side preconditions (checked by the dispatcher): K % 64 == 0; A and B
-// 16-byte aligned with lda, ldb multiples of 8; the m/n-contiguous operand's
-// extent (M if A is transposed, N if B is not) a multiple of 8.  Rows or
+// Host-side preconditions (checked by the dispatcher): A and B 16-byte
+// aligned with lda, ldb multiples of 8; the m/n-contiguous operand's extent
+// (M if A is transposed, N if B is not) a multiple of 8.  A last slab shorter
+// than 64 (K % 64 != 0) is loaded through registers with zero fill.  Rows or
 // columns past M or N are fetched from a clamped, valid address; they only
 // feed outputs that the guarded epilogue never stores.
 #pragma once
@@ -101,6 +102,39 @@ struct PipeOperand {
             }
         }
         step = KCONT ? PIPE_BK : PIPE_BK * ld;
+    }
+
+    // The last slab when K is not a multiple of 64: the same 16-byte pieces
+    // into the same LDS slots, but through registers, with k at or beyond K
+    // read as zero.  Happens once per kernel; the wave waits for these loads.
+    __device__ __forceinline__ void issue_tail(lds_char_t *lds, int wave, int lane, int krem)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
+            int valid;  // halfs of this 16-byte piece that lie before K
+            if constexpr (KCONT) {
+                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> 3);
+                const int c = (lane & 7) ^ ((r >> 1) & 7);
+                valid = krem - c * 8;
+            } else {
+                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
+                valid = r < krem ? 8 : 0;
+            }
+            f16x8 v;
+            if (valid >= 8) {
+                v = *(const f16x8 *)ptr[i];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    _Float16 x = (_Float16)0;
+                    if (e < valid) x = ptr[i][e];
+                    v[e] = x;
+                }
+            }
+            *(lds_f16x8_t *)dst = v;
+            ptr[i] += step;
+        }
     }
 
     // Issue this slab's direct loads into the stage at `lds` and advance.
@@ -191,19 +225,27 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
     int tm, tn;
     tile_coords(blockIdx.x, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = p.K / PIPE_BK;
+    const int nk = (p.K + PIPE_BK - 1) / PIPE_BK;
 
     OpA ga;
     OpB gb;
     ga.init((const _Float16 *)p.A, p.lda, m0, p.M, wave, lane);
     gb.init((const _Float16 *)p.B, p.ldb, n0, p.N, wave, lane);
 
+    // slab s of nk goes through issue_tail when it is a partial last slab
+    const int krem = p.K - (nk - 1) * PIPE_BK;   // k of the last slab (1..64)
+    auto issue_slab = [&](int slab, lds_char_t *st) {
+        if (slab == nk - 1 && krem < PIPE_BK) {
+            ga.issue_tail(st, wave, lane, krem);
+            gb.issue_tail(st + OpA::BYTES, wave, lane, krem);
+        } else {
+            ga.issue(st, wave);
+            gb.issue(st + OpA::BYTES, wave);
+        }
+    };
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) {
-        if (s < nk) {
-            ga.issue(smem + s * STAGE_BYTES, wave);
-            gb.issue(smem + s * STAGE_BYTES + OpA::BYTES, wave);
-        }
+        if (s < nk) issue_slab(s, smem + s * STAGE_BYTES);
     }
 
     f32x16 acc[TM][TN];
@@ -228,8 +270,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
         __syncthreads();
         if (kt + STAGES - 1 < nk) {
             const int ns = (stage == 0 ? STAGES : stage) - 1;   // stage of slab kt-1
-            ga.issue(smem + ns * STAGE_BYTES, wave);
-            gb.issue(smem + ns * STAGE_BYTES + OpA::BYTES, wave);
+            issue_slab(kt + STAGES - 1, smem + ns * STAGE_BYTES);
         }
         const lds_char_t *sA = smem + stage * STAGE_BYTES;
         const lds_char_t *sB = sA + OpA::BYTES;

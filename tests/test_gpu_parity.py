@@ -35,7 +35,7 @@ def kernels_for(dg, dtype):
 
 def pipe_ok(p):
     """Preconditions of the pipelined fp16 kernels (as the header states)."""
-    return (p.K % 64 == 0 and p.lda % 8 == 0 and p.ldb % 8 == 0 and (not p.ta or p.M % 8 == 0)
+    return (p.lda % 8 == 0 and p.ldb % 8 == 0 and (not p.ta or p.M % 8 == 0)
             and (p.tb or p.N % 8 == 0))
 
 
@@ -77,14 +77,17 @@ def test_every_kernel_ragged(dg, dtype, ta, tb, aligned):
 
 @pytest.mark.parametrize("ta,tb", TRANS)
 @pytest.mark.parametrize("shape", [(296, 264, 192), (1000, 1032, 512), (136, 8, 64), (8, 136, 128),
-                                   (264, 520, 256)])
+                                   (264, 520, 256), (264, 136, 32), (136, 264, 100), (200, 144, 1),
+                                   (128, 128, 127), (520, 264, 321)])
 def test_pipelined_f16_kernels(dg, ta, tb, shape):
     """The direct-to-LDS pipelined kernels on shapes meeting their
     preconditions: ragged M and N (clamped loads), one and two K slabs (the
-    pipeline tail), several tiles."""
+    pipeline tail), a partial last K slab (register-loaded, zero-filled),
+    several tiles."""
     M, N, K = shape
     a, b, c0 = synth.problem(M, N, K, "f16", "uniform", 170 + 2 * ta + tb, with_c0=True)
-    p = Problem(a, b, c0, ta, tb, 0.75, 0.5, "f16", (8, 8, 8))
+    pad = tuple((-x) % 8 + 8 for x in ((M if ta else K), (K if tb else N), N))
+    p = Problem(a, b, c0, ta, tb, 0.75, 0.5, "f16", pad)
     assert pipe_ok(p)
     for k in kernels_for(dg, "f16"):
         if "pipe" in dg.dg_kernel_name(k):
