@@ -76,7 +76,9 @@ def time_launches(fn, stream, reps):
 def lora_step(dev, stream, reps):
     """Times the 18 GEMMs of one LoRA MLP-block step (512 tokens, d_model 2048,
     FFN 5632, rank 32; fp16 operands, fp32 accumulation) back to back on one
-    stream, and each GEMM on its own (events around repeated launches)."""
+    stream, and each GEMM on its own (events around repeated launches).  Each
+    GEMM goes through dg_gemm_splitk with the library's choice of K split
+    (skinny and low-rank products are split, the others are not)."""
     import numpy as np
     import torch
 
@@ -85,6 +87,10 @@ def lora_step(dev, stream, reps):
 
     sptr = stream.cuda_stream
     calls = []
+    # one split-K workspace for the whole step (the calls are ordered on one stream)
+    wsb = max(dg.dg_gemm_splitk_workspace_size(M, N, dg.dg_gemm_splitk_choose(ta, tb, M, N, K, 1))
+              for _, M, N, K, ta, tb, _, _ in synth.LORA_GEMMS)
+    ws = torch.empty(max(wsb, 16) // 4, dtype=torch.float32, device=dev)
     for idx, (name, M, N, K, ta, tb, beta, _) in enumerate(synth.LORA_GEMMS):
         a, b, c0 = synth.lora_problem(idx, seed=3)
         A = torch.from_numpy(np.ascontiguousarray(a.T if ta else a)).to(dev)
@@ -94,12 +100,15 @@ def lora_step(dev, stream, reps):
         k = dg.dg_select_kernel(ta, tb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), N,
                                 dg.DG_F16_F32ACC)
 
+        splits = dg.dg_gemm_splitk_choose(ta, tb, M, N, K, dg.DG_F16_F32ACC)
+
         def f(ta=ta, tb=tb, M=M, N=N, K=K, A=A, B=B, C=C, lda=lda, ldb=ldb, beta=beta):
-            rc = dg.dg_gemm(ta, tb, M, N, K, 1.0, A.data_ptr(), lda, B.data_ptr(), ldb, beta,
-                            C.data_ptr(), N, dg.DG_F16_F32ACC, sptr)
+            rc = dg.dg_gemm_splitk(ta, tb, M, N, K, 1.0, A.data_ptr(), lda, B.data_ptr(), ldb, beta,
+                                   C.data_ptr(), N, dg.DG_F16_F32ACC, sptr, 0, ws.data_ptr(),
+                                   ws.numel() * 4)
             if rc != 0:
                 raise dg.GemmError(rc)
-        calls.append((name, M, N, K, f, dg.dg_kernel_name(k)))
+        calls.append((name, M, N, K, f, dg.dg_kernel_name(k) + (f" splitk{splits}" if splits > 1 else "")))
 
     def step():
         for c in calls:

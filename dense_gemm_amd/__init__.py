@@ -5,7 +5,7 @@ arguments: every step of the computation runs in the library's HIP kernels.
 `gemm()` is a convenience over torch tensors (torch is used for device memory
 and streams only).
 
-The library must have been built (python -m dense_gemm_amd.build); importing
+The library must have been built (python dense_gemm_amd/build.py); importing
 this package fails loudly when it is missing.
 """
 from __future__ import annotations
@@ -22,7 +22,7 @@ DG_OK, DG_ERR_UNSUPPORTED, DG_ERR_HIP = 0, -100, -200
 DG_KERNEL_AUTO = -1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m dense_gemm_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python dense_gemm_amd/build.py`")
 
 # torch (the owner of the device memory and streams handed to the library)
 # ships its own HIP runtime.  Load it first so the library's libamdhip64.so.7
@@ -38,6 +38,12 @@ _lib.dg_gemm.argtypes = _GEMM_ARGS
 _lib.dg_gemm.restype = _ci
 _lib.dg_gemm_with_kernel.argtypes = _GEMM_ARGS + [_ci]
 _lib.dg_gemm_with_kernel.restype = _ci
+_lib.dg_gemm_splitk.argtypes = _GEMM_ARGS + [_ci, _vp, ctypes.c_size_t]
+_lib.dg_gemm_splitk.restype = _ci
+_lib.dg_gemm_splitk_choose.argtypes = [_ci, _ci, _i64, _i64, _i64, _ci]
+_lib.dg_gemm_splitk_choose.restype = _ci
+_lib.dg_gemm_splitk_workspace_size.argtypes = [_i64, _i64, _ci]
+_lib.dg_gemm_splitk_workspace_size.restype = ctypes.c_size_t
 _lib.dg_select_kernel.argtypes = [_ci, _ci, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _ci]
 _lib.dg_select_kernel.restype = _ci
 _lib.dg_kernel_count.argtypes = []
@@ -55,7 +61,8 @@ _lib.dg_last_hip_error.restype = _ci
 _lib.dg_version.argtypes = []
 _lib.dg_version.restype = _ci
 
-EXPORTED = ["dg_gemm", "dg_gemm_with_kernel", "dg_select_kernel", "dg_kernel_count",
+EXPORTED = ["dg_gemm", "dg_gemm_with_kernel", "dg_gemm_splitk", "dg_gemm_splitk_choose",
+            "dg_gemm_splitk_workspace_size", "dg_select_kernel", "dg_kernel_count",
             "dg_kernel_name", "dg_kernel_tile_m", "dg_kernel_tile_n", "dg_status_string",
             "dg_last_hip_error", "dg_version"]
 
@@ -91,6 +98,20 @@ def dg_gemm_with_kernel(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
                         stream, kernel) -> int:
     return _lib.dg_gemm_with_kernel(int(transA), int(transB), M, N, K, alpha, A, lda, B, ldb, beta,
                                     C, ldc, int(dtype), stream, int(kernel))
+
+
+def dg_gemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
+                   splits, workspace, workspace_bytes) -> int:
+    return _lib.dg_gemm_splitk(int(transA), int(transB), M, N, K, alpha, A, lda, B, ldb, beta, C,
+                               ldc, int(dtype), stream, int(splits), workspace, int(workspace_bytes))
+
+
+def dg_gemm_splitk_choose(transA, transB, M, N, K, dtype) -> int:
+    return _lib.dg_gemm_splitk_choose(int(transA), int(transB), M, N, K, int(dtype))
+
+
+def dg_gemm_splitk_workspace_size(M, N, splits) -> int:
+    return _lib.dg_gemm_splitk_workspace_size(M, N, int(splits))
 
 
 def dg_select_kernel(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, dtype) -> int:

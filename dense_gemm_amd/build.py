@@ -1,6 +1,8 @@
 """Build libdense_gemm_amd.so for gfx950 with hipcc, in place.
 
-    python -m dense_gemm_amd.build
+    python dense_gemm_amd/build.py
+
+(run by path: importing the package would load the library being rebuilt)
 
 Each source compiles to an object in _build/ (in parallel), then one link.
 """

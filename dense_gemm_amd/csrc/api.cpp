@@ -11,6 +11,7 @@
 namespace dg {
 launch_fn simple_launcher(int dtype, int ta, int tb);
 launch_fn scale_launcher(int dtype);
+launch_fn splitk_reduce_launcher(int dtype);
 const launch_fn *f32_launchers(int config);
 const launch_fn *f16_launchers(int config);
 const launch_fn *f16_pipe_launchers(int config);
@@ -131,9 +132,25 @@ bool supports(int kernel, int ta, int tb, int64_t M, int64_t N, int64_t K, const
     return ceil_div(M, f.bm) * ceil_div(N, f.bn) <= 0x7fffffff;
 }
 
+// Number of K splits for a problem whose output has `tiles` tiles: enough
+// workgroups to cover the 256 compute units, at least 4 K slabs of 64 per
+// split; no split once half the compute units have a tile, nor for K below
+// 1024, where the reduction's launch costs more than the split saves
+// (measured on the LoRA step's K = 512 products).
+int splits_for(int64_t tiles, int64_t K)
+{
+    if (tiles >= 128 || K < 1024) return 1;
+    const int64_t want = ceil_div(256, tiles);
+    const int64_t slabs = ceil_div(K, 64);
+    int64_t s = slabs / 4;
+    if (s > want) s = want;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
 int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
         const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype, void *stream,
-        int kernel)
+        int kernel, int splits = 1, void *ws = nullptr, size_t ws_bytes = 0)
 {
     int rc = validate(ta, tb, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
     if (rc) return rc;
@@ -156,6 +173,9 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     p.tiles_m = p.tiles_n = 0;
     p.group_m = 1;
     p.c_vec = aligned16(C) && ldc % (dtype == DG_F32 ? 4 : 8) == 0;
+    p.splits = 1;
+    p.k_chunk = 0;
+    p.ws = nullptr;
     hipStream_t s = (hipStream_t)stream;
     const int di = dtype == DG_F32 ? 0 : 1;
 
@@ -172,8 +192,21 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
             p.tiles_m = (int32_t)ceil_div(M, f.bm);
             p.tiles_n = (int32_t)ceil_div(N, f.bn);
             p.group_m = f.group_m;
+            if (splits == 0) splits = splits_for((int64_t)p.tiles_m * p.tiles_n, K);
+            if (splits > 1) {
+                // k_chunk: a multiple of 64 (every kernel's K slab divides it)
+                p.k_chunk = (int32_t)(ceil_div(ceil_div(K, splits), 64) * 64);
+                p.splits = (int32_t)ceil_div(K, p.k_chunk);
+                if (p.splits > 1) {
+                    if ((size_t)p.splits * (size_t)M * (size_t)N * 4 > ws_bytes) return -18;
+                    p.ws = (float *)ws;
+                } else {
+                    p.k_chunk = 0;
+                }
+            }
             const int v = (f.kind == PIPE || vec_ok(A, lda, B, ldb, dtype)) ? 0 : 4;
             err = f.variants(f.config)[v + ta * 2 + tb](p, s);
+            if (err == hipSuccess && p.splits > 1) err = dg::splitk_reduce_launcher(di)(p, s);
         }
     }
     if (err != hipSuccess) {
@@ -201,6 +234,40 @@ int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K,
 {
     return run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
                kernel);
+}
+
+int dg_gemm_splitk(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                   const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
+                   int64_t ldc, int dtype, void *stream, int splits, void *workspace,
+                   size_t workspace_bytes)
+{
+    int rc = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
+    if (rc) return rc;
+    if (splits < 0 || splits > 4096) return -16;
+    if (splits != 1 && M > 0 && N > 0 && (workspace == nullptr || !aligned16(workspace))) return -17;
+    return run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
+               DG_KERNEL_AUTO, splits, workspace, workspace_bytes);
+}
+
+int dg_gemm_splitk_choose(int transA, int transB, int64_t M, int64_t N, int64_t K, int dtype)
+{
+    int rc = validate(transA, transB, M, N, K, 1.f, nullptr, transA ? (M > 1 ? M : 1) : (K > 1 ? K : 1),
+                      nullptr, transB ? (K > 1 ? K : 1) : (N > 1 ? N : 1), nullptr, N > 1 ? N : 1,
+                      dtype, false);
+    if (rc) return rc;
+    if (M == 0 || N == 0 || K == 0) return 1;
+    // the tile of the kernel dg_gemm would pick for aligned operands
+    const int k = choose(transA, transB, M, N, K, (const void *)256, transA ? ((M + 7) / 8) * 8 : ((K + 7) / 8) * 8,
+                         (const void *)256, transB ? ((K + 7) / 8) * 8 : ((N + 7) / 8) * 8, dtype);
+    const Family &f = kFamilies[k];
+    if (f.kind == SIMPLE) return 1;
+    return splits_for(ceil_div(M, f.bm) * ceil_div(N, f.bn), K);
+}
+
+size_t dg_gemm_splitk_workspace_size(int64_t M, int64_t N, int splits)
+{
+    if (M <= 0 || N <= 0 || splits <= 1) return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * 4;
 }
 
 int dg_select_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
@@ -250,6 +317,9 @@ const char *dg_status_string(int status)
     case -13: return "invalid ldc";
     case -14: return "invalid dtype";
     case -15: return "invalid stream";
+    case -16: return "invalid splits";
+    case -17: return "invalid workspace (NULL or not 16-byte aligned)";
+    case -18: return "workspace too small";
     default: return "unknown status";
     }
 }

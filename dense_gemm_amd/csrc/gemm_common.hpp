@@ -22,12 +22,36 @@ struct GemmParams {
     int32_t tiles_m, tiles_n;  // output tiles of the launch
     int32_t group_m;           // tile rows walked together (cache locality)
     int32_t c_vec;             // C rows start on 16-byte boundaries (16-byte stores allowed)
+    // split-K: with splits > 1 the grid is tiles x splits; workgroup (tile, s)
+    // covers k in [s*k_chunk, min(K, (s+1)*k_chunk)) and writes its raw fp32
+    // sums to ws[s][M][N] (row stride N) instead of C.
+    int32_t splits;
+    int32_t k_chunk;           // a multiple of every kernel's K slab
+    float *ws;
 };
 
 // A host-side launcher: enqueues one kernel on `stream`, returns a hipError_t.
 typedef hipError_t (*launch_fn)(const GemmParams &p, hipStream_t stream);
 
 #ifdef __HIPCC__
+// Workgroup id -> (split, id of the tile within the split) and the split's
+// k range [k_begin, k_begin + k_len).
+__device__ __forceinline__ void split_of(const GemmParams &p, int &bid, int &split, int &k_begin,
+                                         int &k_len)
+{
+    bid = blockIdx.x;
+    split = 0;
+    k_begin = 0;
+    k_len = p.K;
+    if (p.splits > 1) {
+        const int ntiles = p.tiles_m * p.tiles_n;
+        split = bid / ntiles;
+        bid -= split * ntiles;
+        k_begin = split * p.k_chunk;
+        k_len = p.K - k_begin < p.k_chunk ? p.K - k_begin : p.k_chunk;
+    }
+}
+
 // Workgroup id -> output tile (tm, tn).
 //
 // The hardware hands consecutive workgroup ids to the 8 XCDs in turn

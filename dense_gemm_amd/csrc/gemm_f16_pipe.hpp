@@ -222,18 +222,23 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
     const int wm0 = (wq / WAVES_N) * WM;
     const int wn0 = (wq % WAVES_N) * WN;
     const int kk0 = kgroup * KPW;
+    int bid, split, k_begin, Kl;
+    split_of(p, bid, split, k_begin, Kl);
     int tm, tn;
-    tile_coords(blockIdx.x, p, tm, tn);
+    tile_coords(bid, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = (p.K + PIPE_BK - 1) / PIPE_BK;
+    const int nk = (Kl + PIPE_BK - 1) / PIPE_BK;
 
+    // this split's k range starts at k_begin (a multiple of 64)
     OpA ga;
     OpB gb;
-    ga.init((const _Float16 *)p.A, p.lda, m0, p.M, wave, lane);
-    gb.init((const _Float16 *)p.B, p.ldb, n0, p.N, wave, lane);
+    ga.init((const _Float16 *)p.A + (TA ? (int64_t)k_begin * p.lda : (int64_t)k_begin), p.lda, m0, p.M,
+            wave, lane);
+    gb.init((const _Float16 *)p.B + (TB ? (int64_t)k_begin : (int64_t)k_begin * p.ldb), p.ldb, n0, p.N,
+            wave, lane);
 
     // slab s of nk goes through issue_tail when it is a partial last slab
-    const int krem = p.K - (nk - 1) * PIPE_BK;   // k of the last slab (1..64)
+    const int krem = Kl - (nk - 1) * PIPE_BK;    // k of the last slab (1..64)
     auto issue_slab = [&](int slab, lds_char_t *st) {
         if (slab == nk - 1 && krem < PIPE_BK) {
             ga.issue_tail(st, wave, lane, krem);
@@ -361,12 +366,28 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
         for (int c4 = 0; c4 < 4; ++c4) {
             const f32x4 x = *(const lds_f32x4_t *)(stg + (lr * EPI_LD + lc + 4 * c4) * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * c4 + e] = p.alpha * x[e];
+            for (int e = 0; e < 4; ++e) v[4 * c4 + e] = x[e];
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the slot is rewritten
         __builtin_amdgcn_wave_barrier();
         const int grow = m0 + wm0 + 32 * i + lr;
         const int gcol = n0 + wn0 + 32 * j + lc;
+        if (p.splits > 1) {
+            // raw fp32 partial sums of this split
+            float *w = p.ws + ((int64_t)split * p.M + grow) * p.N + gcol;
+            if (grow < p.M && gcol + 16 <= p.N && (p.N & 3) == 0) {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    *(f32x4 *)(w + 4 * c4) = (f32x4){v[4 * c4], v[4 * c4 + 1], v[4 * c4 + 2], v[4 * c4 + 3]};
+            } else if (grow < p.M) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (gcol + e < p.N) w[e] = v[e];
+            }
+            continue;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] *= p.alpha;
         _Float16 *c = C + (int64_t)grow * p.ldc + gcol;
         if (p.c_vec && grow < p.M && gcol + 16 <= p.N) {
             if (p.beta != 0.f) {
@@ -401,7 +422,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
 template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
 hipError_t launch_f16_pipe(const GemmParams &p, hipStream_t s)
 {
-    const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+    const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
     return hipLaunchKernel((const void *)&gemm_f16_pipe_kernel<BM, BN, WM, WN, TA, TB, STAGES, KSPLIT>,

@@ -183,22 +183,25 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
     constexpr int STAGE = OpA::ELEMS + OpB::ELEMS;
     __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
 
-    const T *A = (const T *)p.A;
-    const T *B = (const T *)p.B;
+    int bid, split, k_begin, Kl;
+    split_of(p, bid, split, k_begin, Kl);
+    // this split's k range starts at k_begin: offset the operands to it
+    const T *A = (const T *)p.A + (TA ? (int64_t)k_begin * p.lda : (int64_t)k_begin);
+    const T *B = (const T *)p.B + (TB ? (int64_t)k_begin : (int64_t)k_begin * p.ldb);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM;
     const int wn0 = (wave % WAVES_N) * WN;
     int tm, tn;
-    tile_coords(blockIdx.x, p, tm, tn);
+    tile_coords(bid, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = (p.K + BK - 1) / BK;
+    const int nk = (Kl + BK - 1) / BK;
 
     OpA ga;
     OpB gb;
-    ga.load(A, p.lda, m0, 0, p.M, p.K, tid);
-    gb.load(B, p.ldb, n0, 0, p.N, p.K, tid);
+    ga.load(A, p.lda, m0, 0, p.M, Kl, tid);
+    gb.load(B, p.ldb, n0, 0, p.N, Kl, tid);
     ga.store(smem, tid);
     gb.store(smem + OpA::ELEMS, tid);
     __syncthreads();
@@ -220,8 +223,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
         const T *sB = sA + OpA::ELEMS;
         const bool more = kt + 1 < nk;
         if (more) {
-            ga.load(A, p.lda, m0, (kt + 1) * BK, p.M, p.K, tid);
-            gb.load(B, p.ldb, n0, (kt + 1) * BK, p.N, p.K, tid);
+            ga.load(A, p.lda, m0, (kt + 1) * BK, p.M, Kl, tid);
+            gb.load(B, p.ldb, n0, (kt + 1) * BK, p.N, Kl, tid);
         }
         if constexpr (!F16) {
             // fp32: 32x32x2 MFMA, BK/2 steps; 4 steps per chunk
@@ -301,7 +304,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + lrow4 + (r & 3);
-                if (row < p.M) {
+                if (row < p.M && p.splits > 1) {
+                    p.ws[((int64_t)split * p.M + row) * p.N + col] = acc[i][j][r];
+                } else if (row < p.M) {
                     T *c = C + (int64_t)row * p.ldc + col;
                     float v = p.alpha * acc[i][j][r];
                     if (p.beta != 0.f) v = __builtin_fmaf(p.beta, (float)*c, v);
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
 template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VEC, int MINW>
 hipError_t launch_mfma(const GemmParams &p, hipStream_t s)
 {
-    const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+    const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
     return hipLaunchKernel((const void *)&gemm_mfma_kernel<T, BM, BN, BK, WM, WN, TA, TB, VEC, MINW>,

@@ -115,6 +115,57 @@ __global__ __launch_bounds__(256) void scale_c_kernel(GemmParams p)
     }
 }
 
+// Split-K reduction: C = alpha * sum_s ws[s] + beta * C (ws[s] is M x N,
+// row stride N; splits summed in increasing s), one rounding to T.  beta == 0
+// does not read C.  Four consecutive columns per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p)
+{
+    T *C = (T *)p.C;
+    const int64_t mn = (int64_t)p.M * p.N;
+    const int64_t groups = (mn + 3) / 4;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * 256) {
+        const int64_t e0 = g * 4;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if ((p.N & 3) == 0) {
+            for (int sp = 0; sp < p.splits; ++sp) {
+                const f32x4 x = *(const f32x4 *)(p.ws + sp * mn + e0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[u] += x[u];
+            }
+        } else {
+            for (int sp = 0; sp < p.splits; ++sp)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (e0 + u < mn) acc[u] += p.ws[sp * mn + e0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t e = e0 + u;
+            if (e < mn) {
+                const int64_t i = e / p.N, j = e - i * p.N;
+                T *c = C + i * p.ldc + j;
+                float v = p.alpha * acc[u];
+                if (p.beta != 0.f) v = __builtin_fmaf(p.beta, to_f32(*c), v);
+                *c = (T)v;
+            }
+        }
+    }
+}
+
+template <typename T>
+hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t s)
+{
+    const int64_t groups = ((int64_t)p.M * p.N + 3) / 4;
+    int64_t blocks = (groups + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    GemmParams arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel((const void *)&splitk_reduce_kernel<T>, dim3((unsigned)blocks), dim3(256),
+                           args, 0, s);
+}
+
 template <typename T, bool TA, bool TB>
 hipError_t launch_simple(const GemmParams &p, hipStream_t s)
 {
@@ -148,6 +199,11 @@ launch_fn simple_launcher(int dtype, int ta, int tb)
          {launch_simple<_Float16, true, false>, launch_simple<_Float16, true, true>}},
     };
     return table[dtype][ta][tb];
+}
+
+launch_fn splitk_reduce_launcher(int dtype)
+{
+    return dtype == 0 ? launch_splitk_reduce<float> : launch_splitk_reduce<_Float16>;
 }
 
 launch_fn scale_launcher(int dtype)

@@ -63,6 +63,7 @@
 #ifndef DENSE_GEMM_H
 #define DENSE_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -92,6 +93,40 @@ int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha
 int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
                         void *C, int64_t ldc, int dtype, void *stream, int kernel);
+
+/* Split-K form of dg_gemm, for outputs too small to give every compute unit a
+ * tile (skinny and low-rank products): K is cut into `splits` ranges (each a
+ * multiple of 64 long except the last), each range's products are summed
+ * into fp32 partials in `workspace`, and a second kernel forms
+ * C = alpha * (sum of the partials, in increasing range order) + beta * C with
+ * one rounding to the output type.  This is the split-K remedy of "Metal
+ * GEMM Kernels for LoRA Training on Apple Silicon", section 5 (fp32 partials,
+ * then a reduction).
+ *   splits      1: exactly dg_gemm (workspace unused); 0: the library's
+ *               choice (dg_gemm_splitk_choose); n > 1: at most n ranges (the
+ *               range length is rounded up to a multiple of 64, so fewer
+ *               ranges may result).  Invalid (-16): below 0 or above 4096.
+ *   workspace   device memory of at least dg_gemm_splitk_workspace_size(M,
+ *               N, splits) bytes, 16-byte aligned, owned by the caller, not
+ *               read or written outside that size; its contents on return
+ *               are unspecified.  Invalid (-17): NULL or misaligned when
+ *               splits != 1 and the output is not empty.  Too small for the
+ *               ranges actually used: -18.  Two calls that share a workspace
+ *               must be ordered on one stream.
+ * Otherwise as dg_gemm (arguments 1-15, same errors, asynchronous). */
+int dg_gemm_splitk(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                   const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
+                   int64_t ldc, int dtype, void *stream, int splits, void *workspace,
+                   size_t workspace_bytes);
+
+/* The number of K ranges dg_gemm_splitk uses when called with splits = 0
+ * (1 when splitting does not pay), or a negative status for invalid
+ * arguments (host logic only). */
+int dg_gemm_splitk_choose(int transA, int transB, int64_t M, int64_t N, int64_t K, int dtype);
+
+/* Bytes of workspace dg_gemm_splitk needs for `splits` K ranges (0 when
+ * splits <= 1 or the output is empty). */
+size_t dg_gemm_splitk_workspace_size(int64_t M, int64_t N, int splits);
 
 /* The kernel dg_gemm would run for these arguments (host logic only, no GPU
  * call), or a negative status as dg_gemm would return it. */

@@ -141,3 +141,32 @@ def test_status_strings():
     assert dg.dg_status_string(12345) == "unknown status"
     assert dg.dg_last_hip_error() == 0
     assert dg.dg_version() >= 100
+
+
+def test_splitk_host_logic():
+    # the library's choice: split only grids that leave compute units idle
+    assert dg.dg_gemm_splitk_choose(0, 0, 512, 32, 5632, 1) > 1          # LoRA dGa
+    assert dg.dg_gemm_splitk_choose(0, 0, 4096, 4096, 4096, 0) == 1
+    assert dg.dg_gemm_splitk_choose(0, 0, 512, 32, 64, 1) == 1            # too little K
+    assert dg.dg_gemm_splitk_choose(2, 0, 512, 32, 64, 1) == -1
+    assert dg.dg_gemm_splitk_workspace_size(512, 32, 22) == 22 * 512 * 32 * 4
+    assert dg.dg_gemm_splitk_workspace_size(512, 32, 1) == 0
+    assert dg.dg_gemm_splitk_workspace_size(0, 32, 4) == 0
+
+
+def test_splitk_invalid_arguments():
+    def sk(**kw):
+        a = dict(GOOD, splits=2, ws=0x10000, wsb=1 << 20)
+        a.update(kw)
+        return dg.dg_gemm_splitk(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"],
+                                 a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"],
+                                 a["dtype"], a["stream"], a["splits"], a["ws"], a["wsb"])
+    assert sk(ta=3) == -1                       # dg_gemm's checks come first
+    assert sk(splits=-1) == -16
+    assert sk(splits=5000) == -16
+    assert sk(ws=None) == -17
+    assert sk(ws=0x10004) == -17                # not 16-byte aligned
+    # a workspace too small for the ranges used: rejected before any launch
+    assert sk(M=512, N=32, K=5632, lda=5632, ldb=32, ldc=32, splits=8, wsb=1024) == -18
+    assert sk(M=0, ws=None) == 0                # empty output: nothing to do
+    assert dg.dg_status_string(-18) == "workspace too small"

@@ -270,6 +270,59 @@ def test_lora_step_gemm(dg, index):
         check_sampled(p, n=2000, seed=index)
 
 
+# ---------------------------------------------------------------------------
+# split-K: fp32 partials in a caller workspace, then one reduction
+# ---------------------------------------------------------------------------
+def run_splitk(dg, p, splits):
+    import torch
+    dev = torch.device("cuda:0")
+    dtype = torch.float32 if p.dtype == "f32" else torch.float16
+    A = torch.from_numpy(np.ascontiguousarray(p.A)).to(dev)
+    B = torch.from_numpy(np.ascontiguousarray(p.B)).to(dev)
+    C = torch.from_numpy(np.ascontiguousarray(p.C0)).to(dev)
+    n = splits if splits > 0 else max(1, dg.dg_gemm_splitk_choose(p.ta, p.tb, p.M, p.N, p.K, DT[p.dtype]))
+    wsb = max(16, dg.dg_gemm_splitk_workspace_size(p.M, p.N, n))
+    ws = torch.full((wsb // 4,), float("nan"), dtype=torch.float32, device=dev)
+    rc = dg.dg_gemm_splitk(p.ta, p.tb, p.M, p.N, p.K, p.alpha, A.data_ptr(), p.lda, B.data_ptr(),
+                           p.ldb, p.beta, C.data_ptr(), p.ldc, DT[p.dtype],
+                           torch.cuda.current_stream().cuda_stream, splits, ws.data_ptr(), wsb)
+    if rc != 0:
+        raise dg.GemmError(rc)
+    torch.cuda.synchronize()
+    assert C.dtype == dtype
+    return C.cpu().numpy()
+
+
+DT = {"f32": 0, "f16": 1}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("ta,tb", TRANS)
+@pytest.mark.parametrize("shape,splits", [((200, 40, 1000), 0), ((72, 264, 777), 3), ((136, 32, 640), 7),
+                                          ((96, 96, 64), 2), ((520, 48, 2048), 0)])
+def test_splitk(dg, dtype, ta, tb, shape, splits):
+    M, N, K = shape
+    a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 180 + 2 * ta + tb, with_c0=True)
+    pad = tuple((-x) % 8 + 8 for x in ((M if ta else K), (K if tb else N), N))
+    p = Problem(a, b, c0, ta, tb, -1.25, 0.5, dtype, pad)
+    out = run_splitk(dg, p, splits)
+    p.check_padding(out)
+    ref, ab = p.oracle_full()
+    worst, bad = oracle.compare(dtype, out[:, :N].astype(np.float64), ref, ab, p.alpha, p.beta, c0)
+    assert bad == 0, f"{bad} elements out of bound, max err/bound {worst:.3g}"
+
+
+@pytest.mark.parametrize("index", [i for i, g in enumerate(synth.LORA_GEMMS) if g[2] == 32 or g[1] == 32])
+def test_lora_skinny_splitk(dg, index):
+    name, M, N, K, ta, tb, beta, _ = synth.LORA_GEMMS[index]
+    a, b, c0 = synth.lora_problem(index, seed=3)
+    p = Problem(a, b, c0, ta, tb, 1.0, beta, "f16")
+    out = run_splitk(dg, p, 0)
+    ref, ab = p.oracle_full()
+    worst, bad = oracle.compare("f16", out[:, :N].astype(np.float64), ref, ab, 1.0, beta, c0)
+    assert bad == 0, f"{name}: {bad} elements out of bound, max err/bound {worst:.3g}"
+
+
 @functools.lru_cache(maxsize=1)
 def ragged_problem(shape):
     M, N, K = shape
