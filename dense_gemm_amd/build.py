@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "gemm_simple.hip", "gemm_f32.hip", "gemm_f16.hip"]
-HEADERS = ["gemm_common.hpp", "gemm_mfma.hpp", "gemm_f16_pipe.hpp"]
+HEADERS = ["gemm_common.hpp", "gemm_mfma.hpp", "gemm_pipe.hpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -15,6 +15,7 @@ launch_fn splitk_reduce_launcher(int dtype);
 const launch_fn *f32_launchers(int config);
 const launch_fn *f16_launchers(int config);
 const launch_fn *f16_pipe_launchers(int config);
+const launch_fn *f32_pipe_launchers(int config);
 }  // namespace dg
 
 namespace {
@@ -28,9 +29,9 @@ thread_local int g_last_hip_error = 0;
 //   SIMPLE: generic fallback, any problem.
 //   MFMA:   register-staged matrix-core kernels, any shape; 8 variants:
 //           transA x transB x (16-byte vector loads or element loads).
-//   PIPE:   fp16 direct-to-LDS pipelined kernels; 4 variants (transA x transB);
-//           need 16-byte aligned A/B with lda, ldb % 8 == 0, and the
-//           m/n-contiguous operand's extent % 8 == 0.
+//   PIPE:   direct-to-LDS pipelined kernels; 4 variants (transA x transB);
+//           need 16-byte aligned rows of A and B, and the m/n-contiguous
+//           operand's extent a multiple of 16 bytes.
 enum Kind { SIMPLE, MFMA, PIPE };
 struct Family {
     const char *name;
@@ -52,11 +53,15 @@ const Family kFamilies[] = {
     {"f16_128x128_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0},
     {"f16_256x128_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1},
     {"f16_128x128_pipe2_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 2},
+    {"f32_256x128_pipe3_mfma32x32x2", DG_F32, 256, 128, 8, PIPE, dg::f32_pipe_launchers, 0},
+    {"f32_256x256_pipe4_w8_mfma32x32x2", DG_F32, 256, 256, 4, PIPE, dg::f32_pipe_launchers, 1},
+    {"f32_128x128_pipe4_mfma32x32x2", DG_F32, 128, 128, 8, PIPE, dg::f32_pipe_launchers, 2},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
     K_F32_SIMPLE = 0, K_F16_SIMPLE = 1, K_F32_256 = 2, K_F32_128 = 3, K_F16_128 = 4, K_F16_256 = 5,
-    K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7, K_F16_PIPE_128_2 = 8
+    K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7, K_F16_PIPE_128_2 = 8, K_F32_PIPE_256x128 = 9,
+    K_F32_PIPE_256x256 = 10, K_F32_PIPE_128 = 11
 };
 
 constexpr int64_t kMaxDim = 0x7fffffff;
@@ -97,11 +102,15 @@ bool vec_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Preconditions of the pipelined fp16 kernels (see Family).
+// Preconditions of the pipelined kernels (see Family): 16-byte aligned rows
+// of A and B, and the m/n-contiguous operand's extent a whole number of
+// 16-byte pieces.
 bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-             const void *B, int64_t ldb)
+             const void *B, int64_t ldb, int dtype)
 {
-    return vec_ok(A, lda, B, ldb, DG_F16_F32ACC) && (!ta || M % 8 == 0) && (tb || N % 8 == 0);
+    const int64_t v = dtype == DG_F32 ? 4 : 8;
+    (void)K;
+    return vec_ok(A, lda, B, ldb, dtype) && (!ta || M % v == 0) && (tb || N % v == 0);
 }
 
 // Kernel choice by dtype, preconditions and output tile count.  Larger tiles
@@ -110,8 +119,12 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
            const void *B, int64_t ldb, int dtype)
 {
     const int64_t big = ceil_div(M, 256) * ceil_div(N, 128);
-    if (dtype == DG_F32) return big >= 384 ? K_F32_256 : K_F32_128;
-    if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb)) {
+    if (dtype == DG_F32) {
+        if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype))
+            return big >= 384 ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
+        return big >= 384 ? K_F32_256 : K_F32_128;
+    }
+    if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype)) {
         // enough 256x128 tiles for two per CU: the big tile; enough 128x128
         // tiles for two per CU: the shallow two-workgroup pipeline; else the
         // deep one-workgroup pipeline
@@ -128,7 +141,7 @@ bool supports(int kernel, int ta, int tb, int64_t M, int64_t N, int64_t K, const
     const Family &f = kFamilies[kernel];
     if (f.dtype != dtype) return false;
     if (f.kind == SIMPLE) return ceil_div(M, 64) <= 65535;
-    if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb)) return false;
+    if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype)) return false;
     return ceil_div(M, f.bm) * ceil_div(N, f.bn) <= 0x7fffffff;
 }
 

@@ -1,5 +1,5 @@
 // fp16-operand, fp32-accumulate kernel instantiations (v_mfma_f32_32x32x16_f16).
-#include "gemm_f16_pipe.hpp"
+#include "gemm_pipe.hpp"
 #include "gemm_mfma.hpp"
 
 namespace dg {
@@ -33,12 +33,12 @@ const launch_fn *f16_launchers(int config)
 const launch_fn *f16_pipe_launchers(int config)
 {
     static const launch_fn table[3][4] = {
-        {launch_f16_pipe<128, 128, 64, 64, false, false, 4, 2>, launch_f16_pipe<128, 128, 64, 64, false, true, 4, 2>,
-         launch_f16_pipe<128, 128, 64, 64, true, false, 4, 2>, launch_f16_pipe<128, 128, 64, 64, true, true, 4, 2>},
-        {launch_f16_pipe<256, 128, 64, 64, false, false, 2, 1>, launch_f16_pipe<256, 128, 64, 64, false, true, 2, 1>,
-         launch_f16_pipe<256, 128, 64, 64, true, false, 2, 1>, launch_f16_pipe<256, 128, 64, 64, true, true, 2, 1>},
-        {launch_f16_pipe<128, 128, 64, 64, false, false, 2, 2>, launch_f16_pipe<128, 128, 64, 64, false, true, 2, 2>,
-         launch_f16_pipe<128, 128, 64, 64, true, false, 2, 2>, launch_f16_pipe<128, 128, 64, 64, true, true, 2, 2>},
+        {launch_pipe<_Float16, 128, 128, 64, 64, false, false, 4, 2>, launch_pipe<_Float16, 128, 128, 64, 64, false, true, 4, 2>,
+         launch_pipe<_Float16, 128, 128, 64, 64, true, false, 4, 2>, launch_pipe<_Float16, 128, 128, 64, 64, true, true, 4, 2>},
+        {launch_pipe<_Float16, 256, 128, 64, 64, false, false, 2, 1>, launch_pipe<_Float16, 256, 128, 64, 64, false, true, 2, 1>,
+         launch_pipe<_Float16, 256, 128, 64, 64, true, false, 2, 1>, launch_pipe<_Float16, 256, 128, 64, 64, true, true, 2, 1>},
+        {launch_pipe<_Float16, 128, 128, 64, 64, false, false, 2, 2>, launch_pipe<_Float16, 128, 128, 64, 64, false, true, 2, 2>,
+         launch_pipe<_Float16, 128, 128, 64, 64, true, false, 2, 2>, launch_pipe<_Float16, 128, 128, 64, 64, true, true, 2, 2>},
     };
     return table[config];
 }

@@ -1,5 +1,6 @@
 // fp32 matrix-core kernel instantiations (v_mfma_f32_32x32x2_f32).
 #include "gemm_mfma.hpp"
+#include "gemm_pipe.hpp"
 
 namespace dg {
 
@@ -21,6 +22,23 @@ const launch_fn *f32_launchers(int config)
     static const launch_fn table[2][8] = {
         DG_VARIANTS(float, 256, 128, 16, 128, 64, 2),
         DG_VARIANTS(float, 128, 128, 16, 64, 64, 2),
+    };
+    return table[config];
+}
+
+// pipelined direct-to-LDS kernels: [config][transA * 2 + transB]
+//   0: 256x128 tile, 3 stages, 4 waves of 128x64 (two workgroups per CU)
+//   1: 256x256 tile, 4 stages, 8 waves of 128x64 (one workgroup per CU)
+//   2: 128x128 tile, 4 stages, 4 waves of 64x64 (two workgroups per CU)
+const launch_fn *f32_pipe_launchers(int config)
+{
+    static const launch_fn table[3][4] = {
+        {launch_pipe<float, 256, 128, 128, 64, false, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, false, true, 3, 1>,
+         launch_pipe<float, 256, 128, 128, 64, true, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, true, true, 3, 1>},
+        {launch_pipe<float, 256, 256, 128, 64, false, false, 4, 1>, launch_pipe<float, 256, 256, 128, 64, false, true, 4, 1>,
+         launch_pipe<float, 256, 256, 128, 64, true, false, 4, 1>, launch_pipe<float, 256, 256, 128, 64, true, true, 4, 1>},
+        {launch_pipe<float, 128, 128, 64, 64, false, false, 4, 1>, launch_pipe<float, 128, 128, 64, 64, false, true, 4, 1>,
+         launch_pipe<float, 128, 128, 64, 64, true, false, 4, 1>, launch_pipe<float, 128, 128, 64, 64, true, true, 4, 1>},
     };
     return table[config];
 }

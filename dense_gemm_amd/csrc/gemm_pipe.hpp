@@ -1,10 +1,11 @@
-// fp16-operand / fp32-accumulate GEMM for gfx950 with a multi-stage LDS ring
-// fed by direct global->LDS loads.
+// GEMM for gfx950 with a multi-stage LDS ring fed by direct global->LDS
+// loads, for fp16 operands (fp32 accumulation) and for fp32.
 //
 //   C[BM x BN tile] = alpha * sum_k op(A)[rows, k] op(B)[k, cols] + beta * C,
-//   v_mfma_f32_32x32x16_f16 with fp32 accumulators ("Metal GEMM Kernels for
-//   LoRA Training on Apple Silicon", section 1: the fp32 accumulator keeps the
-//   fast path).
+//   fp16: v_mfma_f32_32x32x16_f16 with fp32 accumulators ("Metal GEMM Kernels
+//   for LoRA Training on Apple Silicon", section 1: the fp32 accumulator keeps
+//   the fast path), K slabs of 64;
+//   fp32: v_mfma_f32_32x32x2_f32, K slabs of 16.
 //
 // Why a different kernel from gemm_mfma.hpp: at 2048^3 one 128 x 128 tile per
 // compute unit leaves a single wave per SIMD, and one 64-wide K slab is only
@@ -13,7 +14,7 @@
 // (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane),
 // which costs no registers and no transposing VALU work.
 //
-// LDS layouts (both conflict-free for the fragment reads):
+// fp16 LDS layouts (both conflict-free for the fragment reads):
 //   k-contiguous operand (A not transposed, B transposed): [BMN][64] halfs,
 //     128-byte rows; the 16-byte chunk c of row r sits at chunk c ^ ((r>>1)&7),
 //     so the 16 rows read together by a quarter wave hit 16 distinct bank
@@ -26,6 +27,13 @@
 //     own m (or n) -- the MFMA operand layout -- with no write-side transpose
 //     (the page's section 3 transposes on the write; gfx950 can do it on the
 //     read).
+// fp32 LDS layouts: k-contiguous operand [BMN][16] floats, 64-byte rows, the
+// 16-byte chunk c of row r at chunk c ^ ((r>>2)&3); one ds_read_b128 gives a
+// lane 4 consecutive k (4 MFMA steps).  m/n-contiguous operand [16][BMN]
+// floats, the 128-byte chunk q of row k at q ^ ((k>>3)&1); a lane reads one
+// float per MFMA step, the two half-waves from rows k and k+8 (different
+// bank halves after the swizzle).  In both types lane half h of MFMA step s
+// takes k = h*BK/2 + s, the same for both operands.
 // The swizzle is applied by choosing which global address each lane fetches,
 // since a direct load writes its lanes contiguously.
 //
@@ -37,12 +45,14 @@
 //   reads with MFMAs, measured slower: it drains the MFMA queue mid-slab.)
 //
 // Host-side preconditions (checked by the dispatcher): A and B 16-byte
-// aligned with lda, ldb multiples of 8; the m/n-contiguous operand's extent
-// (M if A is transposed, N if B is not) a multiple of 8.  A last slab shorter
-// than 64 (K % 64 != 0) is loaded through registers with zero fill.  Rows or
+// aligned with lda, ldb multiples of 16 bytes; the m/n-contiguous operand's
+// extent (M if A is transposed, N if B is not) a multiple of 16 bytes.  A
+// last slab shorter than BK is loaded through registers with zero fill.  Rows or
 // columns past M or N are fetched from a clamped, valid address; they only
 // feed outputs that the guarded epilogue never stores.
 #pragma once
+
+#include <type_traits>
 
 #include "gemm_common.hpp"
 
@@ -65,10 +75,11 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One operand of the pipelined kernel.
+// One fp16 operand of the pipelined kernel (K slab 64).
 //   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
 template <int BMN, bool KCONT, int NW>
-struct PipeOperand {
+struct PipeOperandH {
+    static constexpr int BK = PIPE_BK;
     static constexpr int BYTES = BMN * PIPE_BK * 2;      // one stage
     static constexpr int LOADS = BYTES / (NW * 64 * 16);  // 16-byte loads per thread per slab
     static_assert(LOADS * NW * 64 * 16 == BYTES, "slab must split into 16-byte loads");
@@ -181,6 +192,113 @@ struct PipeOperand {
     }
 };
 
+
+// One fp32 operand of the pipelined kernel (K slab 16).
+//   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
+template <int BMN, bool KCONT, int NW>
+struct PipeOperandS {
+    static constexpr int BK = 16;
+    static constexpr int BYTES = BMN * BK * 4;            // one stage
+    static constexpr int LOADS = BYTES / (NW * 64 * 16);  // 16-byte loads per thread per slab
+    static_assert(LOADS * NW * 64 * 16 == BYTES, "slab must split into 16-byte loads");
+    static constexpr int ROW_BYTES = KCONT ? BK * 4 : BMN * 4;
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
+    static_assert(ROWS_PER_LOAD >= 1, "rows of at most 1 KiB");
+
+    const float *ptr[LOADS];
+    int64_t step;
+
+    __device__ __forceinline__ void init(const float *g, int64_t ld, int mn0, int ext, int wave,
+                                         int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int rbase = (i * NW + wave) * ROWS_PER_LOAD;
+            if constexpr (KCONT) {
+                const int r = rbase + (lane >> 2);
+                const int c = (lane & 3) ^ ((r >> 2) & 3);    // logical 16-byte chunk (4 k)
+                int row = mn0 + r;
+                row = row < ext ? row : ext - 1;
+                ptr[i] = g + (int64_t)row * ld + c * 4;
+            } else {
+                const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
+                const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
+                const int q = (p >> 3) ^ ((r >> 3) & 1);          // logical 128-byte chunk
+                int col = mn0 + q * 32 + (p & 7) * 4;
+                col = col < ext ? col : ext - 4;
+                ptr[i] = g + (int64_t)r * ld + col;
+            }
+        }
+        step = KCONT ? BK : BK * ld;
+    }
+
+    __device__ __forceinline__ void issue_tail(lds_char_t *lds, int wave, int lane, int krem)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
+            int valid;  // floats of this 16-byte piece that lie before K
+            if constexpr (KCONT) {
+                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> 2);
+                const int c = (lane & 3) ^ ((r >> 2) & 3);
+                valid = krem - c * 4;
+            } else {
+                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
+                valid = r < krem ? 4 : 0;
+            }
+            f32x4 v;
+            if (valid >= 4) {
+                v = *(const f32x4 *)ptr[i];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = 0.f;
+                    if (e < valid) x = ptr[i][e];
+                    v[e] = x;
+                }
+            }
+            *(__attribute__((address_space(3))) f32x4 *)dst = v;
+            ptr[i] += step;
+        }
+    }
+
+    __device__ __forceinline__ void issue(lds_char_t *lds, int wave)
+    {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                         : "memory");
+            ptr[i] += step;
+        }
+    }
+
+    // The operand values of MFMA steps 4*c2 .. 4*c2+3 for block rows
+    // [b0, b0+32): lane l holds row (or column) b0 + l%32 and
+    // k = (l/32)*8 + 4*c2 + e, e = 0..3.
+    __device__ __forceinline__ f32x4 frag4(const lds_char_t *lds, int b0, int c2, int lane) const
+    {
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+        typedef __attribute__((address_space(3))) float lds_float_t;
+        const int h = lane >> 5;
+        if constexpr (KCONT) {
+            const int r = b0 + (lane & 31);
+            const int c = 2 * h + c2;
+            const int p = c ^ ((r >> 2) & 3);
+            return *(const lds_f32x4_t *)(lds + r * ROW_BYTES + p * 16);
+        } else {
+            const int q = (b0 >> 5) ^ h;   // (k >> 3) & 1 == h for k = 8h + ...
+            const lds_char_t *base = lds + (8 * h + 4 * c2) * ROW_BYTES + q * 128 + (lane & 31) * 4;
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = *(const lds_float_t *)(base + e * ROW_BYTES);
+            return v;
+        }
+    }
+};
+
 // Waves: (BM/WM) x (BN/WN) sub-tiles per K group, KSPLIT groups.  Group g
 // runs the 16-k steps [g*4/KSPLIT, (g+1)*4/KSPLIT) of every slab, so with a
 // 128 x 128 tile of 64 x 64 sub-tiles and KSPLIT = 2 each SIMD holds two
@@ -190,20 +308,23 @@ struct PipeOperand {
 // wave keeps half of its blocks and hands the other half to its partner (the
 // same sub-tile in the other group).  A 256 x 128 tile gets its two waves per
 // SIMD from eight 64 x 64 sub-tiles instead (KSPLIT = 1).
-template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
-__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f16_pipe_kernel(GemmParams p)
+template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_pipe_kernel(GemmParams p)
 {
+    constexpr bool F16 = sizeof(T) == 2;
     constexpr int WAVES_N = BN / WN;
     constexpr int NWG = (BM / WM) * WAVES_N;       // waves per K group
     constexpr int NW = NWG * KSPLIT;               // waves per workgroup
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int NB = TM * TN;                    // 32x32 blocks per wave
-    constexpr int KPW = (PIPE_BK / 16) / KSPLIT;   // 16-k steps per wave per slab
+    constexpr int KPW = (PIPE_BK / 16) / KSPLIT;   // fp16: 16-k steps per wave per slab
     static_assert(KPW >= 1 && KPW * KSPLIT == PIPE_BK / 16, "K split");
     static_assert(KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
-    typedef PipeOperand<BM, !TA, NW> OpA;
-    typedef PipeOperand<BN, TB, NW> OpB;
+    static_assert(F16 || KSPLIT == 1, "fp32 runs without K groups");
+    typedef typename std::conditional<F16, PipeOperandH<BM, !TA, NW>, PipeOperandS<BM, !TA, NW>>::type OpA;
+    typedef typename std::conditional<F16, PipeOperandH<BN, TB, NW>, PipeOperandS<BN, TB, NW>>::type OpB;
+    constexpr int BK = OpA::BK;
     constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
     constexpr int SMEM = STAGES * STAGE_BYTES;
     constexpr int XCHG_BYTES = NW * (NB / 2) * 4096;     // partner exchange
@@ -227,20 +348,20 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
     int tm, tn;
     tile_coords(bid, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = (Kl + PIPE_BK - 1) / PIPE_BK;
+    const int nk = (Kl + BK - 1) / BK;
 
-    // this split's k range starts at k_begin (a multiple of 64)
+    // this split's k range starts at k_begin (a multiple of the slab)
     OpA ga;
     OpB gb;
-    ga.init((const _Float16 *)p.A + (TA ? (int64_t)k_begin * p.lda : (int64_t)k_begin), p.lda, m0, p.M,
+    ga.init((const T *)p.A + (TA ? (int64_t)k_begin * p.lda : (int64_t)k_begin), p.lda, m0, p.M,
             wave, lane);
-    gb.init((const _Float16 *)p.B + (TB ? (int64_t)k_begin : (int64_t)k_begin * p.ldb), p.ldb, n0, p.N,
+    gb.init((const T *)p.B + (TB ? (int64_t)k_begin : (int64_t)k_begin * p.ldb), p.ldb, n0, p.N,
             wave, lane);
 
     // slab s of nk goes through issue_tail when it is a partial last slab
-    const int krem = Kl - (nk - 1) * PIPE_BK;    // k of the last slab (1..64)
+    const int krem = Kl - (nk - 1) * BK;         // k of the last slab (1..BK)
     auto issue_slab = [&](int slab, lds_char_t *st) {
-        if (slab == nk - 1 && krem < PIPE_BK) {
+        if (slab == nk - 1 && krem < BK) {
             ga.issue_tail(st, wave, lane, krem);
             gb.issue_tail(st + OpA::BYTES, wave, lane, krem);
         } else {
@@ -279,19 +400,38 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
         }
         const lds_char_t *sA = smem + stage * STAGE_BYTES;
         const lds_char_t *sB = sA + OpA::BYTES;
+        if constexpr (F16) {
 #pragma unroll
-        for (int s = 0; s < KPW; ++s) {
-            const int kk = kk0 + s;
-            f16x8 a[TM], b[TN];
+            for (int s = 0; s < KPW; ++s) {
+                const int kk = kk0 + s;
+                f16x8 a[TM], b[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = ga.frag(sA, wm0 + 32 * i, kk, lane);
+                for (int i = 0; i < TM; ++i) a[i] = ga.frag(sA, wm0 + 32 * i, kk, lane);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) b[j] = gb.frag(sB, wn0 + 32 * j, kk, lane);
+                for (int j = 0; j < TN; ++j) b[j] = gb.frag(sB, wn0 + 32 * j, kk, lane);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        } else {
+            // 8 MFMA steps of k = 2 per slab, fragments 4 steps at a time
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                f32x4 a[TM], b[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) a[i] = ga.frag4(sA, wm0 + 32 * i, c2, lane);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) b[j] = gb.frag4(sB, wn0 + 32 * j, c2, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+            }
         }
         stage = (stage + 1 == STAGES) ? 0 : stage + 1;
     }
@@ -344,7 +484,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
     // columns 16*(l%2) .. +15, and writes them with two 16-byte stores (one
     // rounding to fp16 per element), or element by element at the matrix
     // edge or when C rows are not 16-byte aligned.
-    _Float16 *C = (_Float16 *)p.C;
+    T *C = (T *)p.C;
     lds_char_t *stg = smem + wave * 32 * EPI_LD * 4;
     typedef __attribute__((address_space(3))) float lds_float_t;
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
@@ -388,44 +528,57 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 1) void gemm_f
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) v[e] *= p.alpha;
-        _Float16 *c = C + (int64_t)grow * p.ldc + gcol;
+        T *c = C + (int64_t)grow * p.ldc + gcol;
         if (p.c_vec && grow < p.M && gcol + 16 <= p.N) {
-            if (p.beta != 0.f) {
-                const f16x8 c0 = *(const f16x8 *)c, c1 = *(const f16x8 *)(c + 8);
+            if constexpr (F16) {
+                if (p.beta != 0.f) {
+                    const f16x8 c0 = *(const f16x8 *)c, c1 = *(const f16x8 *)(c + 8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        v[e] = __builtin_fmaf(p.beta, (float)c0[e], v[e]);
+                        v[8 + e] = __builtin_fmaf(p.beta, (float)c1[e], v[8 + e]);
+                    }
+                }
+                f16x8 o0, o1;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    v[e] = __builtin_fmaf(p.beta, (float)c0[e], v[e]);
-                    v[8 + e] = __builtin_fmaf(p.beta, (float)c1[e], v[8 + e]);
+                    o0[e] = (_Float16)v[e];
+                    o1[e] = (_Float16)v[8 + e];
+                }
+                *(f16x8 *)c = o0;
+                *(f16x8 *)(c + 8) = o1;
+            } else {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    f32x4 o = {v[4 * c4], v[4 * c4 + 1], v[4 * c4 + 2], v[4 * c4 + 3]};
+                    if (p.beta != 0.f) {
+                        const f32x4 ci = *(const f32x4 *)(c + 4 * c4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(p.beta, ci[e], o[e]);
+                    }
+                    *(f32x4 *)(c + 4 * c4) = o;
                 }
             }
-            f16x8 o0, o1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o0[e] = (_Float16)v[e];
-                o1[e] = (_Float16)v[8 + e];
-            }
-            *(f16x8 *)c = o0;
-            *(f16x8 *)(c + 8) = o1;
         } else if (grow < p.M) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 if (gcol + e < p.N) {
                     float x = v[e];
                     if (p.beta != 0.f) x = __builtin_fmaf(p.beta, (float)c[e], x);
-                    c[e] = (_Float16)x;
+                    c[e] = (T)x;
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
-hipError_t launch_f16_pipe(const GemmParams &p, hipStream_t s)
+template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
+hipError_t launch_pipe(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_f16_pipe_kernel<BM, BN, WM, WN, TA, TB, STAGES, KSPLIT>,
+    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT>,
                            dim3(nwg), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
 }
 

@@ -34,9 +34,11 @@ def kernels_for(dg, dtype):
 
 
 def pipe_ok(p):
-    """Preconditions of the pipelined fp16 kernels (as the header states)."""
-    return (p.lda % 8 == 0 and p.ldb % 8 == 0 and (not p.ta or p.M % 8 == 0)
-            and (p.tb or p.N % 8 == 0))
+    """Preconditions of the pipelined kernels: 16-byte rows of A and B, and
+    the m/n-contiguous operand's extent a whole number of 16-byte pieces."""
+    v = 4 if p.dtype == "f32" else 8
+    return (p.lda % v == 0 and p.ldb % v == 0 and (not p.ta or p.M % v == 0)
+            and (p.tb or p.N % v == 0))
 
 
 def run_or_unsupported(dg, p, k, **kw):
@@ -75,21 +77,25 @@ def test_every_kernel_ragged(dg, dtype, ta, tb, aligned):
             check_full(p, kernel=k, out=out)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
 @pytest.mark.parametrize("ta,tb", TRANS)
 @pytest.mark.parametrize("shape", [(296, 264, 192), (1000, 1032, 512), (136, 8, 64), (8, 136, 128),
                                    (264, 520, 256), (264, 136, 32), (136, 264, 100), (200, 144, 1),
-                                   (128, 128, 127), (520, 264, 321)])
-def test_pipelined_f16_kernels(dg, ta, tb, shape):
+                                   (128, 128, 127), (520, 264, 321), (300, 260, 17)])
+def test_pipelined_kernels(dg, dtype, ta, tb, shape):
     """The direct-to-LDS pipelined kernels on shapes meeting their
     preconditions: ragged M and N (clamped loads), one and two K slabs (the
     pipeline tail), a partial last K slab (register-loaded, zero-filled),
     several tiles."""
     M, N, K = shape
-    a, b, c0 = synth.problem(M, N, K, "f16", "uniform", 170 + 2 * ta + tb, with_c0=True)
+    a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 170 + 2 * ta + tb, with_c0=True)
+    v = 4 if dtype == "f32" else 8
+    if (ta and M % v) or (not tb and N % v):
+        pytest.skip("m/n-contiguous extent not a whole number of 16-byte pieces")
     pad = tuple((-x) % 8 + 8 for x in ((M if ta else K), (K if tb else N), N))
-    p = Problem(a, b, c0, ta, tb, 0.75, 0.5, "f16", pad)
+    p = Problem(a, b, c0, ta, tb, 0.75, 0.5, dtype, pad)
     assert pipe_ok(p)
-    for k in kernels_for(dg, "f16"):
+    for k in kernels_for(dg, dtype):
         if "pipe" in dg.dg_kernel_name(k):
             print(f"kernel {dg.dg_kernel_name(k)} {shape} ta={ta} tb={tb}", flush=True)
             check_full(p, kernel=k)
