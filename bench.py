@@ -35,10 +35,11 @@ def tflops(M, N, K, seconds):
     return 2.0 * M * N * K / seconds / 1e12
 
 
-def measured_traffic(dtype, kernel, ta, tb, vec=True):
-    """HBM bytes per dispatch of this kernel from the committed counter summary
-    (profiles/hbm_traffic.txt), or None when that summary was taken from other
-    kernel sources than the ones built now."""
+def measured_traffic(kernel, ta, tb, M, N):
+    """HBM bytes per dispatch of this kernel on an M x N output from the
+    committed counter summary (profiles/hbm_traffic.txt, keyed by kernel,
+    transpose pair and workgroup count), or None when that summary was taken
+    from other kernel sources than the ones built now."""
     import hashlib
     import glob
     import dense_gemm_amd as dg
@@ -55,8 +56,9 @@ def measured_traffic(dtype, kernel, ta, tb, vec=True):
             table[k.strip()] = v.strip()
     if table.get("sources") != h.hexdigest()[:16]:
         return None
-    key = (f"{dtype} {dg.dg_kernel_tile_m(kernel)}x{dg.dg_kernel_tile_n(kernel)} "
-           f"{'t' if ta else 'n'}{'t' if tb else 'n'} {'vec' if vec else 'novec'}")
+    tm, tn = dg.dg_kernel_tile_m(kernel), dg.dg_kernel_tile_n(kernel)
+    wgs = -(-M // tm) * -(-N // tn)
+    key = f"{dg.dg_kernel_name(kernel)} {'t' if ta else 'n'}{'t' if tb else 'n'} wgs={wgs}"
     return int(float(table[key])) if key in table else None
 
 
@@ -210,7 +212,7 @@ def main():
                    "M": M, "N": N, "K": K, "kernel": dg.dg_kernel_name(kernel)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32, 4),
-                     "traffic": measured_traffic("f32", kernel, 0, 0),
+                     "traffic": measured_traffic(kernel, 0, 0, M, N),
                      "algorithmic_bytes": 3 * M * N * 4, "kernel_ms": round(launch_s * 1e3, 4)},
     }
 
@@ -239,7 +241,9 @@ def main():
             t16 = min(time_launches(step16, stream, reps) for _ in range(3))
             ach = tflops(S, S, S, t16)
             res[name] = {"tflops": round(ach, 2), "frac": round(ach / PEAK_F16, 4),
-                         "kernel_us": round(t16 * 1e6, 2), "kernel": dg.dg_kernel_name(k16)}
+                         "kernel_us": round(t16 * 1e6, 2), "kernel": dg.dg_kernel_name(k16),
+                         "traffic": measured_traffic(k16, ta, tb, S, S),
+                         "algorithmic_bytes": 3 * S * S * 2}
         out["fp16_2048"] = {"peak": PEAK_F16, "unit": "TFLOP/s", **res}
 
     # ---- LoRA MLP-block step: the 18 fp16 GEMMs of one forward + backward -------
