@@ -37,12 +37,17 @@
 // The swizzle is applied by choosing which global address each lane fetches,
 // since a direct load writes its lanes contiguously.
 //
-// Pipeline per K slab kt (one barrier per slab):
-//   wait for this thread's loads of slab kt; barrier (slab kt visible to all,
-//   and everyone is done reading slab kt-1); issue the loads of slab
-//   kt+STAGES-1 into the stage slab kt-1 used; MFMAs on slab kt.  (Moving the
-//   barrier into the middle of a slab, to overlap the next slab's first LDS
-//   reads with MFMAs, measured slower: it drains the MFMA queue mid-slab.)
+// Pipeline per K slab kt (one barrier per slab), fp16:
+//   wait for this thread's loads of slab kt+1; barrier (slab kt+1 visible to
+//   all, and every wave holds its fragments of slab kt in registers); issue
+//   the loads of slab kt+STAGES into the stage slab kt used; read the
+//   fragments of slab kt+1 into the second register set while the MFMAs of
+//   slab kt run.  fp32 (whose larger wave tiles leave no registers for a
+//   second fragment set): wait for slab kt; barrier; issue slab kt+STAGES-1
+//   into the stage of slab kt-1; fragment reads and MFMAs of slab kt.
+//   (Moving the barrier into the middle of a slab, to overlap the next slab's
+//   first LDS reads with MFMAs, measured slower: it drains the MFMA queue
+//   mid-slab.)
 //
 // Host-side preconditions (checked by the dispatcher): A and B 16-byte
 // aligned with lda, ldb multiples of 16 bytes; the m/n-contiguous operand's
@@ -369,8 +374,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             gb.issue(st + OpA::BYTES, wave);
         }
     };
+    // fp16 keeps STAGES slabs in flight, fp32 STAGES - 1 (see the loops below)
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
+    for (int s = 0; s < (F16 ? STAGES : STAGES - 1); ++s) {
         if (s < nk) issue_slab(s, smem + s * STAGE_BYTES);
     }
 
@@ -384,38 +390,67 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 acc[i][j][r] = 0.f;
 
     constexpr int LOADS = OpA::LOADS + OpB::LOADS;
-    // One barrier per slab, at its start: slab kt is then in LDS for every
-    // wave and every wave is done with slab kt-1, whose stage receives the
-    // loads of slab kt+STAGES-1.  The slab's MFMAs follow, the compiler
-    // interleaving the fragment reads with them; a wave waiting at the next
-    // barrier still has its last MFMAs in flight.
-    int stage = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * LOADS>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        if (kt + STAGES - 1 < nk) {
-            const int ns = (stage == 0 ? STAGES : stage) - 1;   // stage of slab kt-1
-            issue_slab(kt + STAGES - 1, smem + ns * STAGE_BYTES);
-        }
-        const lds_char_t *sA = smem + stage * STAGE_BYTES;
-        const lds_char_t *sB = sA + OpA::BYTES;
-        if constexpr (F16) {
+    if constexpr (F16) {
+        // Two fragment sets, the loop unrolled by two so that each set stays
+        // in fixed registers.  The next slab's LDS reads are unconditional:
+        // after the last slab they read a stale stage that is never used, so
+        // that no branch separates them from the MFMAs (the compiler's LDS
+        // wait bookkeeping would otherwise wait for them before the MFMAs).
+        f16x8 fa0[KPW][TM], fb0[KPW][TN], fa1[KPW][TM], fb1[KPW][TN];
+        auto read = [&](int slab, f16x8(&fa)[KPW][TM], f16x8(&fb)[KPW][TN]) {
+            const lds_char_t *sA = smem + (slab % STAGES) * STAGE_BYTES;
+            const lds_char_t *sB = sA + OpA::BYTES;
 #pragma unroll
             for (int s = 0; s < KPW; ++s) {
-                const int kk = kk0 + s;
-                f16x8 a[TM], b[TN];
 #pragma unroll
-                for (int i = 0; i < TM; ++i) a[i] = ga.frag(sA, wm0 + 32 * i, kk, lane);
+                for (int i = 0; i < TM; ++i) fa[s][i] = ga.frag(sA, wm0 + 32 * i, kk0 + s, lane);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) b[j] = gb.frag(sB, wn0 + 32 * j, kk, lane);
+                for (int j = 0; j < TN; ++j) fb[s][j] = gb.frag(sB, wn0 + 32 * j, kk0 + s, lane);
+            }
+        };
+        auto step = [&](int kt, f16x8(&ca)[KPW][TM], f16x8(&cb)[KPW][TN], f16x8(&na)[KPW][TM],
+                        f16x8(&nb)[KPW][TN]) {
+            // slabs issued so far: [0, min(nk, kt + STAGES)); slab kt+1 must be complete
+            if (kt + STAGES <= nk) wait_vmcnt<(STAGES - 2) * LOADS>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (kt + STAGES < nk) issue_slab(kt + STAGES, smem + (kt % STAGES) * STAGE_BYTES);
+            read(kt + 1, na, nb);
+#pragma unroll
+            for (int s = 0; s < KPW; ++s)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ca[s][i], cb[s][j], acc[i][j], 0, 0, 0);
+        };
+        if (nk > 0) {
+            if (nk >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            read(0, fa0, fb0);
+        }
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, fa0, fb0, fa1, fb1);
+            if (kt + 1 < nk) step(kt + 1, fa1, fb1, fa0, fb0);
+        }
+    } else {
+        // One barrier per slab, at its start: slab kt is then in LDS for
+        // every wave and every wave is done with slab kt-1, whose stage
+        // receives the loads of slab kt+STAGES-1.  The slab's MFMAs follow,
+        // the compiler interleaving the fragment reads with them; a wave
+        // waiting at the next barrier still has its last MFMAs in flight.
+        int stage = 0;
+        for (int kt = 0; kt < nk; ++kt) {
+            if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * LOADS>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (kt + STAGES - 1 < nk) {
+                const int ns = (stage == 0 ? STAGES : stage) - 1;   // stage of slab kt-1
+                issue_slab(kt + STAGES - 1, smem + ns * STAGE_BYTES);
             }
-        } else {
+            const lds_char_t *sA = smem + stage * STAGE_BYTES;
+            const lds_char_t *sB = sA + OpA::BYTES;
             // 8 MFMA steps of k = 2 per slab, fragments 4 steps at a time
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
@@ -432,8 +467,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                         for (int j = 0; j < TN; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
             }
+            stage = (stage + 1 == STAGES) ? 0 : stage + 1;
         }
-        stage = (stage + 1 == STAGES) ? 0 : stage + 1;
     }
 
     // ---- sum the K groups' partial accumulators (KSPLIT == 2) ---------------
