@@ -21,7 +21,11 @@ _SRC = os.path.join(_HERE, "oracle_gemm.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-_TYPE = {np.dtype(np.float32): 0, np.dtype(np.float16): 1, np.dtype(np.float64): 2}
+# element types of the C oracle; bf16 matrices are held as uint16 bit patterns
+_TYPE = {np.dtype(np.float32): 0, np.dtype(np.float16): 1, np.dtype(np.float64): 2,
+         np.dtype(np.uint16): 3}
+
+ACT = {"none": 0, "relu": 1, "gelu": 2}
 
 
 def build(force: bool = True) -> str:
@@ -45,8 +49,17 @@ def bind(path: str):
     lib.oracle_gemm_points.argtypes = [ci, ci, i64, i64, i64, dbl, vp, i64, ci, vp, i64, ci,
                                        dbl, vp, i64, ci, i64, vp, vp, vp, vp, ci]
     lib.oracle_gemm_points.restype = ci
+    lib.oracle_gemm_ex.argtypes = [ci, ci, i64, i64, i64, dbl, vp, i64, i64, ci, vp, i64, i64, ci,
+                                   dbl, vp, i64, i64, ci, vp, ci, ci, i64, vp, vp, vp, ci]
+    lib.oracle_gemm_ex.restype = ci
+    lib.oracle_gemm_points_ex.argtypes = [ci, ci, i64, i64, i64, dbl, vp, i64, i64, ci, vp, i64,
+                                          i64, ci, dbl, vp, i64, i64, ci, vp, ci, ci, i64, vp, vp,
+                                          vp, vp, vp, vp, ci]
+    lib.oracle_gemm_points_ex.restype = ci
     lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_f16_to_f64.restype = dbl
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = dbl
     return lib
 
 
@@ -112,15 +125,87 @@ def gemm_points(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float
     return ref, absum
 
 
+def gemm_ex(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float, A, lda: int,
+            B, ldb: int, beta: float, C0, ldc: int, bias=None, act: str = "none", batch: int = 1,
+            strideA: int = 0, strideB: int = 0, strideC: int = 0, nthreads: int = 0):
+    """Oracle of act(alpha*op(A)op(B) + beta*C0 + bias) over a strided batch.
+    A, B, C0 are flat or 2-D stored buffers holding every batch (batch b at
+    element offset b*stride); bias has N elements.  bf16 buffers are uint16
+    bit patterns.  Returns (ref, pre, absum), each batch x M x N fp64 (pre is
+    the value before the activation)."""
+    lib = _load()
+    for a, n in ((A, "A"), (B, "B"), (C0, "C0"), (bias, "bias")):
+        _check(a, n)
+    ref = np.empty((batch, M, N), dtype=np.float64)
+    pre = np.empty((batch, M, N), dtype=np.float64)
+    absum = np.empty((batch, M, N), dtype=np.float64)
+    tc = _TYPE[C0.dtype] if C0 is not None else 2
+    tbias = _TYPE[bias.dtype] if bias is not None else 2
+    rc = lib.oracle_gemm_ex(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda,
+                            strideA, _TYPE[A.dtype], _ptr(B), ldb, strideB, _TYPE[B.dtype],
+                            float(beta), _ptr(C0), ldc, strideC, tc, _ptr(bias), tbias, ACT[act],
+                            batch, ref.ctypes.data, pre.ctypes.data, absum.ctypes.data,
+                            int(nthreads))
+    if rc < 0:
+        raise RuntimeError(f"oracle_gemm_ex failed ({rc})")
+    return ref, pre, absum
+
+
+def gemm_points_ex(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float, A, lda, B,
+                   ldb, beta: float, C0, ldc, batches, rows, cols, bias=None, act: str = "none",
+                   strideA: int = 0, strideB: int = 0, strideC: int = 0, nthreads: int = 0):
+    """Oracle (ref, pre, absum) at the elements (batches[p], rows[p], cols[p])."""
+    lib = _load()
+    for a, n in ((A, "A"), (B, "B"), (C0, "C0"), (bias, "bias")):
+        _check(a, n)
+    pb = np.ascontiguousarray(batches, dtype=np.int64)
+    pi = np.ascontiguousarray(rows, dtype=np.int64)
+    pj = np.ascontiguousarray(cols, dtype=np.int64)
+    n = pi.shape[0]
+    ref, pre, absum = (np.empty(n, dtype=np.float64) for _ in range(3))
+    tc = _TYPE[C0.dtype] if C0 is not None else 2
+    tbias = _TYPE[bias.dtype] if bias is not None else 2
+    rc = lib.oracle_gemm_points_ex(int(transA), int(transB), M, N, K, float(alpha), _ptr(A), lda,
+                                   strideA, _TYPE[A.dtype], _ptr(B), ldb, strideB, _TYPE[B.dtype],
+                                   float(beta), _ptr(C0), ldc, strideC, tc, _ptr(bias), tbias,
+                                   ACT[act], n, pb.ctypes.data, pi.ctypes.data, pj.ctypes.data,
+                                   ref.ctypes.data, pre.ctypes.data, absum.ctypes.data,
+                                   int(nthreads))
+    if rc < 0:
+        raise RuntimeError(f"oracle_gemm_points_ex failed ({rc})")
+    return ref, pre, absum
+
+
 def f16_to_f64(bits: int) -> float:
     return _load().oracle_f16_to_f64(bits)
+
+
+def bf16_to_f64(bits: int) -> float:
+    return _load().oracle_bf16_to_f64(bits)
+
+
+def values(buf) -> np.ndarray:
+    """fp64 values of a stored buffer (bf16 given as uint16 bit patterns): the
+    magnitudes the error bound needs (|beta * C0|, |bias|).  bf16 is the upper
+    half of an fp32 encoding, so its value is that fp32 number."""
+    buf = np.asarray(buf)
+    if buf.dtype == np.uint16:
+        return (buf.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return buf.astype(np.float64)
 
 
 # ---------------------------------------------------------------------------
 # Error bound of the comparison
 # ---------------------------------------------------------------------------
-RTOL = {"f32": 2e-5, "f16": 2e-3}
-ATOL = {"f32": 1e-6, "f16": 1e-4}
+# fp32 and fp16-in/fp32-acc as stated; bf16 operands also multiply exactly in
+# fp32 (8 x 8 significant bits) and accumulate in fp32, so they take the fp16
+# path's bound, with the output rounding of bf16.
+RTOL = {"f32": 2e-5, "f16": 2e-3, "bf16": 2e-3}
+ATOL = {"f32": 1e-6, "f16": 1e-4, "bf16": 1e-4}
+# largest slope of gelu(x) = x Phi(x): at x = sqrt(2), Phi(sqrt 2) + sqrt(2) phi(sqrt 2)
+GELU_LIPSCHITZ = 1.129
+# fp32 evaluation of gelu: erf to a few ulp of 1, times |x|/2
+GELU_ABS = 1e-6
 
 
 def half_ulp_f16(x: np.ndarray) -> np.ndarray:
@@ -135,33 +220,63 @@ def half_ulp_f16(x: np.ndarray) -> np.ndarray:
     return 0.5 * sp
 
 
-def bound(dtype: str, ref, absum, alpha: float, beta: float, c0_logical=None) -> np.ndarray:
-    """|C - ref| <= rtol * (|alpha| * absum + |beta * C0|) + atol (+ fp16 half-ulp).
+BF16_MAX = 3.3895313892515355e38   # (2 - 2^-7) * 2^127
+
+
+def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 numbers at |x|: 2^(e-9) for |x| in
+    [2^(e-1), 2^e), 2^-134 among subnormals; infinite past the overflow
+    threshold (the output is then an infinity, compared as such)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(ax)
+    h = np.ldexp(1.0, np.maximum(e - 9, -134))
+    # values that round past the largest finite bf16 overflow
+    return np.where(ax >= BF16_MAX + np.ldexp(1.0, 119), np.inf, h)
+
+
+def half_ulp_out(dtype: str, x) -> np.ndarray:
+    if dtype == "f16":
+        return half_ulp_f16(x)
+    if dtype == "bf16":
+        return half_ulp_bf16(x)
+    return np.zeros(np.shape(x))
+
+
+def bound(dtype: str, ref, absum, alpha: float, beta: float, c0_logical=None, bias_logical=None,
+          act: str = "none", pre=None) -> np.ndarray:
+    """|C - ref| <= rtol * (|alpha| * absum + |beta * C0| + |bias|) + atol,
+    carried through the activation, plus half an ulp of the output type.
 
     The stated bound is rtol * sum_k |a_ik b_kj| + atol at alpha=1, beta=0;
     with general alpha and beta the sum is scaled by |alpha| and the C0 term
-    |beta * C0| is added.  fp16 outputs are additionally allowed half an fp16
+    |beta * C0| is added; a bias adds its magnitude the same way (one more
+    fp32 addition).  An activation maps an input error e to at most L * e, L
+    its largest slope (relu 1, gelu 1.129, rounded up); gelu's own fp32 evaluation adds
+    GELU_ABS * |x|.  fp16 and bf16 outputs are additionally allowed half an
     ulp of the reference (their final rounding)."""
     extra = 0.0
     if beta != 0.0 and c0_logical is not None:
         extra = np.abs(beta * np.asarray(c0_logical, dtype=np.float64))
+    if bias_logical is not None:
+        extra = extra + np.abs(np.asarray(bias_logical, dtype=np.float64))
     b = RTOL[dtype] * (abs(alpha) * np.asarray(absum) + extra) + ATOL[dtype]
-    if dtype == "f16":
-        b = b + half_ulp_f16(ref)
-    return b
+    if act == "gelu":
+        b = GELU_LIPSCHITZ * b + GELU_ABS * np.abs(np.asarray(pre, dtype=np.float64))
+    return b + half_ulp_out(dtype, ref)
 
 
-def compare(dtype: str, got, ref, absum, alpha: float, beta: float, c0_logical=None):
+def compare(dtype: str, got, ref, absum, alpha: float, beta: float, c0_logical=None,
+            bias_logical=None, act: str = "none", pre=None):
     """Returns (max err/bound, number of violations).  NaN in `got` counts as a
     violation; an infinity passes only where the reference rounds to the same
     infinity in the output type."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    b = bound(dtype, ref, absum, alpha, beta, c0_logical)
+    b = bound(dtype, ref, absum, alpha, beta, c0_logical, bias_logical, act, pre)
     with np.errstate(invalid="ignore", over="ignore"):
         err = np.abs(got - ref)
         inf_ok = np.isinf(got) & np.isinf(b)
-        if dtype == "f16":
+        if dtype in ("f16", "bf16"):
             inf_ok &= (np.sign(got) == np.sign(ref))
         ratio = np.where(inf_ok, 0.0, err / b)
     ratio = np.where(np.isnan(ratio), np.inf, ratio)

@@ -20,7 +20,9 @@ the previous one, so every transpose variant of a shape sees the same logical
 operands.
 
 Rounding: values are drawn in fp64, then rounded once (IEEE round to nearest
-even) to the storage type (fp32 or fp16).
+even) to the storage type (fp32, fp16 or bf16).  numpy has no bf16 type, so
+bf16 matrices are held as their 16-bit patterns (uint16): the upper half of
+the fp32 encoding, 8 significant bits.
 """
 from __future__ import annotations
 
@@ -77,13 +79,38 @@ class Stream:
         return (lo + np.floor(u * (hi - lo + 1))).reshape(shape)
 
 
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bit patterns with one round-to-nearest-even.
+
+    bf16 keeps 8 significant bits over fp32's exponent range: the quantum of
+    a value in [2^(e-1), 2^e) is 2^(e-8), and 2^-133 below 2^-126
+    (subnormals).  The significand in units of the quantum is rounded half to
+    even (np.rint); the rounded value is then exactly an fp32 number whose low
+    16 bits are zero (or an infinity past the largest finite bf16)."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    _, e = np.frexp(ax)
+    q = np.maximum(e - 8, -133)
+    v = np.ldexp(np.rint(np.ldexp(ax, -q)), q)
+    with np.errstate(over="ignore", invalid="ignore"):
+        f = np.where(np.signbit(x), -v, v).astype(np.float32)
+    bits = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
+
+
 def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
-    """One IEEE round-to-nearest-even from fp64 to the storage type."""
+    """One IEEE round-to-nearest-even from fp64 to the storage type (bf16 as
+    uint16 bit patterns)."""
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32)
     if dtype == "f16":
         return np.asarray(x, dtype=np.float64).astype(np.float16)
+    if dtype == "bf16":
+        return _bf16_bits(x)
     raise ValueError(dtype)
+
+
+BF16_NAN = np.uint16(0x7FC0)
 
 
 def store(logical: np.ndarray, trans: bool, ld: int | None = None, pad_value=np.nan) -> tuple[np.ndarray, int]:
@@ -103,7 +130,8 @@ def store(logical: np.ndarray, trans: bool, ld: int | None = None, pad_value=np.
         raise ValueError("ld below the stored column count")
     buf = np.empty((rows, ld), dtype=logical.dtype)
     if ld > cols:
-        buf[:, cols:] = pad_value
+        # bf16 bit patterns: the NaN canary is a bf16 quiet NaN
+        buf[:, cols:] = BF16_NAN if logical.dtype == np.uint16 and pad_value is np.nan else pad_value
     buf[:, :cols] = s
     return buf, ld
 
