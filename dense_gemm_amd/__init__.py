@@ -17,7 +17,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdense_gemm_amd.so")
 
 DG_OP_N, DG_OP_T = 0, 1
-DG_F32, DG_F16_F32ACC = 0, 1
+DG_F32, DG_F16_F32ACC, DG_BF16_F32ACC = 0, 1, 2
+DG_EPI_NONE, DG_EPI_RELU, DG_EPI_GELU = 0, 1, 2
+EPILOGUES = {"none": DG_EPI_NONE, "relu": DG_EPI_RELU, "gelu": DG_EPI_GELU}
 DG_OK, DG_ERR_UNSUPPORTED, DG_ERR_HIP = 0, -100, -200
 DG_KERNEL_AUTO = -1
 
@@ -38,6 +40,12 @@ _lib.dg_gemm.argtypes = _GEMM_ARGS
 _lib.dg_gemm.restype = _ci
 _lib.dg_gemm_with_kernel.argtypes = _GEMM_ARGS + [_ci]
 _lib.dg_gemm_with_kernel.restype = _ci
+_EX_ARGS = [_ci, _ci, _i64, _i64, _i64, _f32, _vp, _i64, _i64, _vp, _i64, _i64, _f32, _vp, _i64,
+            _i64, _i64, _vp, _ci, _ci, _vp]
+_lib.dg_gemm_ex.argtypes = _EX_ARGS
+_lib.dg_gemm_ex.restype = _ci
+_lib.dg_gemm_ex_with_kernel.argtypes = _EX_ARGS + [_ci]
+_lib.dg_gemm_ex_with_kernel.restype = _ci
 _lib.dg_gemm_splitk.argtypes = _GEMM_ARGS + [_ci, _vp, ctypes.c_size_t]
 _lib.dg_gemm_splitk.restype = _ci
 _lib.dg_gemm_splitk_choose.argtypes = [_ci, _ci, _i64, _i64, _i64, _ci]
@@ -61,7 +69,8 @@ _lib.dg_last_hip_error.restype = _ci
 _lib.dg_version.argtypes = []
 _lib.dg_version.restype = _ci
 
-EXPORTED = ["dg_gemm", "dg_gemm_with_kernel", "dg_gemm_splitk", "dg_gemm_splitk_choose",
+EXPORTED = ["dg_gemm", "dg_gemm_with_kernel", "dg_gemm_ex", "dg_gemm_ex_with_kernel", "dg_gemm_splitk",
+            "dg_gemm_splitk_choose",
             "dg_gemm_splitk_workspace_size", "dg_select_kernel", "dg_kernel_count",
             "dg_kernel_name", "dg_kernel_tile_m", "dg_kernel_tile_n", "dg_status_string",
             "dg_last_hip_error", "dg_version"]
@@ -98,6 +107,20 @@ def dg_gemm_with_kernel(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
                         stream, kernel) -> int:
     return _lib.dg_gemm_with_kernel(int(transA), int(transB), M, N, K, alpha, A, lda, B, ldb, beta,
                                     C, ldc, int(dtype), stream, int(kernel))
+
+
+def dg_gemm_ex(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+               strideC, batch, bias, epilogue, dtype, stream) -> int:
+    return _lib.dg_gemm_ex(int(transA), int(transB), M, N, K, alpha, A, lda, strideA, B, ldb,
+                           strideB, beta, C, ldc, strideC, batch, bias, int(epilogue), int(dtype),
+                           stream)
+
+
+def dg_gemm_ex_with_kernel(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta,
+                           C, ldc, strideC, batch, bias, epilogue, dtype, stream, kernel) -> int:
+    return _lib.dg_gemm_ex_with_kernel(int(transA), int(transB), M, N, K, alpha, A, lda, strideA, B,
+                                       ldb, strideB, beta, C, ldc, strideC, batch, bias,
+                                       int(epilogue), int(dtype), stream, int(kernel))
 
 
 def dg_gemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
@@ -155,47 +178,68 @@ def kernel_names() -> list[str]:
 # ---- torch convenience -------------------------------------------------------
 def _dtype_code(t):
     import torch
-    if t.dtype == torch.float32:
-        return DG_F32
-    if t.dtype == torch.float16:
-        return DG_F16_F32ACC
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or float16)")
+    codes = {torch.float32: DG_F32, torch.float16: DG_F16_F32ACC, torch.bfloat16: DG_BF16_F32ACC}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32, float16 or bfloat16)")
+    return codes[t.dtype]
 
 
 def _ld(t, name):
-    if t.dim() != 2:
-        raise ValueError(f"{name} must be 2-D")
-    if t.stride(1) != 1 and t.shape[1] > 1:
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
         raise ValueError(f"{name} must have unit column stride (row-major rows)")
-    return max(t.stride(0), t.shape[1], 1)
+    return max(t.stride(-2), t.shape[-1], 1)
 
 
-def gemm(A, B, C=None, transA=False, transB=False, alpha=1.0, beta=0.0, kernel=DG_KERNEL_AUTO,
-         stream=None):
-    """C = alpha * op(A) @ op(B) + beta * C on torch CUDA (HIP) tensors.
+def _batch_stride(t, batch, name):
+    """Element stride between the matrices of a 3-D operand (0 for a 2-D one,
+    which every batch then shares)."""
+    if t.dim() == 2:
+        return 0
+    if t.dim() != 3 or t.shape[0] != batch:
+        raise ValueError(f"{name} must be 2-D or [{batch}, rows, cols]")
+    return t.stride(0) if batch > 1 else 0
+
+
+def gemm(A, B, C=None, transA=False, transB=False, alpha=1.0, beta=0.0, bias=None,
+         activation="none", kernel=DG_KERNEL_AUTO, stream=None):
+    """C = act(alpha * op(A) @ op(B) + beta * C + bias) on torch CUDA (HIP)
+    tensors, for one matrix or a strided batch.
 
     A is [M, K] (or [K, M] with transA), B is [K, N] (or [N, K] with transB);
-    all row-major with unit column stride; ld comes from stride(0).  C is
-    allocated (uninitialised, so beta must be 0) when None.  Runs on the
-    current torch stream unless `stream` (a torch stream) is given."""
+    either may carry a leading batch dimension (a 2-D operand is shared by
+    every batch); all row-major with unit column stride, ld from the row
+    stride.  bias (optional) has N elements of C's dtype; activation is
+    "none", "relu" or "gelu".  C is allocated (uninitialised, so beta must be
+    0) when None.  Runs on the current torch stream unless `stream` (a torch
+    stream) is given."""
     import torch
     dt = _dtype_code(A)
     if B.dtype != A.dtype or (C is not None and C.dtype != A.dtype):
         raise TypeError("A, B and C must share one dtype")
-    M, K = (A.shape[1], A.shape[0]) if transA else (A.shape[0], A.shape[1])
-    Kb, N = (B.shape[1], B.shape[0]) if transB else (B.shape[0], B.shape[1])
+    if bias is not None and (bias.dtype != A.dtype or bias.dim() != 1 or bias.stride(0) != 1):
+        raise TypeError("bias must be a contiguous 1-D tensor of C's dtype")
+    batched = A.dim() == 3 or B.dim() == 3 or (C is not None and C.dim() == 3)
+    batch = max(A.shape[0] if A.dim() == 3 else 1, B.shape[0] if B.dim() == 3 else 1,
+                C.shape[0] if (C is not None and C.dim() == 3) else 1)
+    M, K = (A.shape[-1], A.shape[-2]) if transA else (A.shape[-2], A.shape[-1])
+    Kb, N = (B.shape[-1], B.shape[-2]) if transB else (B.shape[-2], B.shape[-1])
     if Kb != K:
         raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
+    if bias is not None and bias.shape[0] != N:
+        raise ValueError(f"bias must have {N} elements")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
-        C = torch.empty((M, N), dtype=A.dtype, device=A.device)
-    if tuple(C.shape) != (M, N):
-        raise ValueError(f"C must be [{M}, {N}]")
+        C = torch.empty((batch, M, N) if batched else (M, N), dtype=A.dtype, device=A.device)
+    if tuple(C.shape[-2:]) != (M, N) or (batched and (C.dim() != 3 or C.shape[0] != batch)):
+        raise ValueError(f"C must be [{batch}, {M}, {N}]" if batched else f"C must be [{M}, {N}]")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
-    rc = dg_gemm_with_kernel(transA, transB, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"),
-                             B.data_ptr(), _ld(B, "B"), float(beta), C.data_ptr(), _ld(C, "C"), dt,
-                             s.cuda_stream, kernel)
+    sa, sb = _batch_stride(A, batch, "A"), _batch_stride(B, batch, "B")
+    sc = C.stride(0) if (batched and batch > 1) else 0
+    rc = dg_gemm_ex_with_kernel(transA, transB, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"),
+                                sa, B.data_ptr(), _ld(B, "B"), sb, float(beta), C.data_ptr(),
+                                _ld(C, "C"), sc, batch, bias.data_ptr() if bias is not None else None,
+                                EPILOGUES[activation], dt, s.cuda_stream, kernel)
     if rc != DG_OK:
         raise GemmError(rc)
     return C

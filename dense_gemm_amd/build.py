@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libdense_gemm_amd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gemm_simple.hip", "gemm_f32.hip", "gemm_f16.hip"]
+SOURCES = ["api.cpp", "gemm_simple.hip", "gemm_f32.hip", "gemm_f16.hip", "gemm_bf16.hip"]
 HEADERS = ["gemm_common.hpp", "gemm_mfma.hpp", "gemm_pipe.hpp"]
 
 FLAGS = [

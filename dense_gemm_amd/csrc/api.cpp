@@ -16,6 +16,7 @@ const launch_fn *f32_launchers(int config);
 const launch_fn *f16_launchers(int config);
 const launch_fn *f16_pipe_launchers(int config);
 const launch_fn *f32_pipe_launchers(int config);
+const launch_fn *bf16_pipe_launchers(int config);
 }  // namespace dg
 
 namespace {
@@ -56,13 +57,33 @@ const Family kFamilies[] = {
     {"f32_256x128_pipe3_mfma32x32x2", DG_F32, 256, 128, 8, PIPE, dg::f32_pipe_launchers, 0},
     {"f32_256x256_pipe4_w8_mfma32x32x2", DG_F32, 256, 256, 4, PIPE, dg::f32_pipe_launchers, 1},
     {"f32_128x128_pipe4_mfma32x32x2", DG_F32, 128, 128, 8, PIPE, dg::f32_pipe_launchers, 2},
+    {"bf16_64x64_simple", DG_BF16_F32ACC, 64, 64, 1, SIMPLE, nullptr, 0},
+    {"bf16_128x128_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 0},
+    {"bf16_256x128_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1},
+    {"bf16_128x128_pipe2_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 2},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
     K_F32_SIMPLE = 0, K_F16_SIMPLE = 1, K_F32_256 = 2, K_F32_128 = 3, K_F16_128 = 4, K_F16_256 = 5,
     K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7, K_F16_PIPE_128_2 = 8, K_F32_PIPE_256x128 = 9,
-    K_F32_PIPE_256x256 = 10, K_F32_PIPE_128 = 11
+    K_F32_PIPE_256x256 = 10, K_F32_PIPE_128 = 11, K_BF16_SIMPLE = 12, K_BF16_PIPE_128 = 13,
+    K_BF16_PIPE_256 = 14, K_BF16_PIPE_128_2 = 15
 };
+
+constexpr int64_t kMaxBatch = 65535;   // a grid dimension
+
+// The strided-batch and epilogue arguments of dg_gemm_ex (defaults: one
+// matrix, no bias, no activation).
+struct Ext {
+    int64_t sA = 0, sB = 0, sC = 0;
+    int64_t batch = 1;
+    const void *bias = nullptr;
+    int act = DG_EPI_NONE;
+};
+
+bool is_dtype(int dtype) { return dtype == DG_F32 || dtype == DG_F16_F32ACC || dtype == DG_BF16_F32ACC; }
+
+int64_t elem_bytes(int dtype) { return dtype == DG_F32 ? 4 : 2; }
 
 constexpr int64_t kMaxDim = 0x7fffffff;
 
@@ -87,17 +108,48 @@ int validate(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const
     if (ldb < max1(tb == DG_OP_T ? K : N)) return -10;
     if (check_ptrs && M > 0 && N > 0 && C == nullptr) return -12;
     if (ldc < max1(N)) return -13;
-    if (dtype != DG_F32 && dtype != DG_F16_F32ACC) return -14;
+    if (!is_dtype(dtype)) return -14;
     return 0;
+}
+
+// The extended arguments (batch strides, batch count, bias, activation) in
+// dg_gemm_ex's parameter order; returns 0 or -(1-based index there).
+int validate_ext(int64_t M, int64_t N, int64_t ldc, const Ext &x, int dtype)
+{
+    if (x.sA < 0) return -9;
+    if (x.sB < 0) return -12;
+    // batches of C must not overlap: batch b+1 starts past the last element of batch b
+    if (x.sC < 0 || (x.batch > 1 && M > 0 && N > 0 && x.sC < (M - 1) * ldc + N)) return -16;
+    if (x.batch < 0 || x.batch > kMaxBatch) return -17;
+    if (x.bias && ((uintptr_t)x.bias % (uintptr_t)elem_bytes(dtype)) != 0) return -18;
+    if (x.act != DG_EPI_NONE && x.act != DG_EPI_RELU && x.act != DG_EPI_GELU) return -19;
+    return 0;
+}
+
+// dg_gemm's argument position -> dg_gemm_ex's (the extended form inserts the
+// batch strides after lda, ldb and ldc, and batch, bias, epilogue before dtype).
+int ex_position(int rc)
+{
+    switch (rc) {
+    case -9: return -10;    // B
+    case -10: return -11;   // ldb
+    case -11: return -13;   // beta
+    case -12: return -14;   // C
+    case -13: return -15;   // ldc
+    case -14: return -20;   // dtype
+    default: return rc;     // transA .. lda keep their positions
+    }
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-// 16-byte vector loads need every row start of A and B on a 16-byte boundary.
-bool vec_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype)
+// 16-byte vector loads need every row start of A and B on a 16-byte boundary
+// (in every batch: the batch strides are whole 16-byte pieces too).
+bool vec_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype, const Ext &x)
 {
-    const int64_t v = dtype == DG_F32 ? 4 : 8;
-    return aligned16(A) && aligned16(B) && lda % v == 0 && ldb % v == 0;
+    const int64_t v = 16 / elem_bytes(dtype);
+    return aligned16(A) && aligned16(B) && lda % v == 0 && ldb % v == 0 &&
+           (x.batch <= 1 || (x.sA % v == 0 && x.sB % v == 0));
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -106,42 +158,48 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // of A and B, and the m/n-contiguous operand's extent a whole number of
 // 16-byte pieces.
 bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-             const void *B, int64_t ldb, int dtype)
+             const void *B, int64_t ldb, int dtype, const Ext &x)
 {
-    const int64_t v = dtype == DG_F32 ? 4 : 8;
+    const int64_t v = 16 / elem_bytes(dtype);
     (void)K;
-    return vec_ok(A, lda, B, ldb, dtype) && (!ta || M % v == 0) && (tb || N % v == 0);
+    return vec_ok(A, lda, B, ldb, dtype, x) && (!ta || M % v == 0) && (tb || N % v == 0);
 }
 
 // Kernel choice by dtype, preconditions and output tile count.  Larger tiles
 // re-read less of A and B; smaller tiles fill more of the 256 compute units.
 int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-           const void *B, int64_t ldb, int dtype)
+           const void *B, int64_t ldb, int dtype, const Ext &x = Ext())
 {
-    const int64_t big = ceil_div(M, 256) * ceil_div(N, 128);
+    // a batch multiplies the workgroups: count the tiles of all batches
+    const int64_t nb = x.batch > 1 ? x.batch : 1;
+    const int64_t big = ceil_div(M, 256) * ceil_div(N, 128) * nb;
+    const int64_t small = ceil_div(M, 128) * ceil_div(N, 128) * nb;
+    const bool pipe = pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x);
     if (dtype == DG_F32) {
-        if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype))
-            return big >= 384 ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
+        if (pipe) return big >= 384 ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
-    if (pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype)) {
-        // enough 256x128 tiles for two per CU: the big tile; enough 128x128
-        // tiles for two per CU: the shallow two-workgroup pipeline; else the
-        // deep one-workgroup pipeline
-        if (big >= 512) return K_F16_PIPE_256;
-        return ceil_div(M, 128) * ceil_div(N, 128) >= 512 ? K_F16_PIPE_128_2 : K_F16_PIPE_128;
+    // 16-bit operands: enough 256x128 tiles for two per CU: the big tile;
+    // enough 128x128 tiles for two per CU: the shallow two-workgroup
+    // pipeline; else the deep one-workgroup pipeline
+    const bool bf = dtype == DG_BF16_F32ACC;
+    if (pipe) {
+        if (big >= 512) return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
+        if (small >= 512) return bf ? K_BF16_PIPE_128_2 : K_F16_PIPE_128_2;
+        return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
     }
+    if (bf) return K_BF16_SIMPLE;
     return big >= 512 ? K_F16_256 : K_F16_128;
 }
 
 bool supports(int kernel, int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A,
-              int64_t lda, const void *B, int64_t ldb, int dtype)
+              int64_t lda, const void *B, int64_t ldb, int dtype, const Ext &x)
 {
     if (kernel < 0 || kernel >= kNumKernels) return false;
     const Family &f = kFamilies[kernel];
     if (f.dtype != dtype) return false;
     if (f.kind == SIMPLE) return ceil_div(M, 64) <= 65535;
-    if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype)) return false;
+    if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x)) return false;
     return ceil_div(M, f.bm) * ceil_div(N, f.bn) <= 0x7fffffff;
 }
 
@@ -163,11 +221,11 @@ int splits_for(int64_t tiles, int64_t K)
 
 int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
         const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype, void *stream,
-        int kernel, int splits = 1, void *ws = nullptr, size_t ws_bytes = 0)
+        int kernel, int splits = 1, void *ws = nullptr, size_t ws_bytes = 0, const Ext &x = Ext())
 {
-    int rc = validate(ta, tb, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
+    int rc = validate(ta, tb, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype, x.batch > 0);
     if (rc) return rc;
-    if (M == 0 || N == 0) return DG_OK;
+    if (M == 0 || N == 0 || x.batch == 0) return DG_OK;
     if (kernel != DG_KERNEL_AUTO && (kernel < 0 || kernel >= kNumKernels))
         return DG_ERR_UNSUPPORTED;
 
@@ -185,19 +243,26 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     p.beta = beta;
     p.tiles_m = p.tiles_n = 0;
     p.group_m = 1;
-    p.c_vec = aligned16(C) && ldc % (dtype == DG_F32 ? 4 : 8) == 0;
+    const int64_t v = 16 / elem_bytes(dtype);
+    p.c_vec = aligned16(C) && ldc % v == 0 && (x.batch <= 1 || x.sC % v == 0);
     p.splits = 1;
     p.k_chunk = 0;
     p.ws = nullptr;
+    p.bias = x.bias;
+    p.act = x.act;
+    p.strideA = x.sA;
+    p.strideB = x.sB;
+    p.strideC = x.sC;
+    p.batch = (int32_t)x.batch;
     hipStream_t s = (hipStream_t)stream;
-    const int di = dtype == DG_F32 ? 0 : 1;
+    const int di = dtype;   // launcher tables are indexed by dtype
 
     hipError_t err;
     if (K == 0 || alpha == 0.f) {
         err = dg::scale_launcher(di)(p, s);
     } else {
-        if (kernel == DG_KERNEL_AUTO) kernel = choose(ta, tb, M, N, K, A, lda, B, ldb, dtype);
-        if (!supports(kernel, ta, tb, M, N, K, A, lda, B, ldb, dtype)) return DG_ERR_UNSUPPORTED;
+        if (kernel == DG_KERNEL_AUTO) kernel = choose(ta, tb, M, N, K, A, lda, B, ldb, dtype, x);
+        if (!supports(kernel, ta, tb, M, N, K, A, lda, B, ldb, dtype, x)) return DG_ERR_UNSUPPORTED;
         const Family &f = kFamilies[kernel];
         if (f.kind == SIMPLE) {
             err = dg::simple_launcher(di, ta, tb)(p, s);
@@ -217,8 +282,8 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
                     p.k_chunk = 0;
                 }
             }
-            const int v = (f.kind == PIPE || vec_ok(A, lda, B, ldb, dtype)) ? 0 : 4;
-            err = f.variants(f.config)[v + ta * 2 + tb](p, s);
+            const int vi = (f.kind == PIPE || vec_ok(A, lda, B, ldb, dtype, x)) ? 0 : 4;
+            err = f.variants(f.config)[vi + ta * 2 + tb](p, s);
             if (err == hipSuccess && p.splits > 1) err = dg::splitk_reduce_launcher(di)(p, s);
         }
     }
@@ -249,6 +314,39 @@ int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K,
                kernel);
 }
 
+int dg_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+               const void *A, int64_t lda, int64_t strideA, const void *B, int64_t ldb,
+               int64_t strideB, float beta, void *C, int64_t ldc, int64_t strideC,
+               int64_t batch, const void *bias, int epilogue, int dtype, void *stream)
+{
+    return dg_gemm_ex_with_kernel(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                  strideB, beta, C, ldc, strideC, batch, bias, epilogue, dtype,
+                                  stream, DG_KERNEL_AUTO);
+}
+
+int dg_gemm_ex_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                           const void *A, int64_t lda, int64_t strideA, const void *B,
+                           int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc,
+                           int64_t strideC, int64_t batch, const void *bias, int epilogue,
+                           int dtype, void *stream, int kernel)
+{
+    Ext x;
+    x.sA = strideA;
+    x.sB = strideB;
+    x.sC = strideC;
+    x.batch = batch;
+    x.bias = bias;
+    x.act = epilogue;
+    int rc = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype,
+                      batch > 0);
+    if (rc) return ex_position(rc);
+    rc = validate_ext(M, N, ldc, x, dtype);
+    if (rc) return rc;
+    rc = run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream, kernel,
+             1, nullptr, 0, x);
+    return rc < 0 && rc > -100 ? ex_position(rc) : rc;
+}
+
 int dg_gemm_splitk(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
                    const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
                    int64_t ldc, int dtype, void *stream, int splits, void *workspace,
@@ -271,7 +369,7 @@ int dg_gemm_splitk_choose(int transA, int transB, int64_t M, int64_t N, int64_t 
     if (M == 0 || N == 0 || K == 0) return 1;
     // the tile of the kernel dg_gemm would pick for aligned operands
     const int k = choose(transA, transB, M, N, K, (const void *)256, transA ? ((M + 7) / 8) * 8 : ((K + 7) / 8) * 8,
-                         (const void *)256, transB ? ((K + 7) / 8) * 8 : ((N + 7) / 8) * 8, dtype);
+                         (const void *)256, transB ? ((K + 7) / 8) * 8 : ((N + 7) / 8) * 8, dtype, Ext());
     const Family &f = kFamilies[k];
     if (f.kind == SIMPLE) return 1;
     return splits_for(ceil_div(M, f.bm) * ceil_div(N, f.bn), K);
@@ -289,7 +387,7 @@ int dg_select_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, co
 {
     int rc = validate(transA, transB, M, N, K, 1.f, A, lda, B, ldb, C, ldc, dtype, false);
     if (rc) return rc;
-    return choose(transA, transB, M, N, K, A, lda, B, ldb, dtype);
+    return choose(transA, transB, M, N, K, A, lda, B, ldb, dtype, Ext());
 }
 
 int dg_kernel_count(void) { return kNumKernels; }
@@ -315,30 +413,34 @@ const char *dg_status_string(int status)
     case DG_OK: return "ok";
     case DG_ERR_UNSUPPORTED: return "kernel does not support this problem";
     case DG_ERR_HIP: return "HIP error (see dg_last_hip_error)";
-    case -1: return "invalid transA";
-    case -2: return "invalid transB";
-    case -3: return "invalid M";
-    case -4: return "invalid N";
-    case -5: return "invalid K";
-    case -6: return "invalid alpha";
-    case -7: return "invalid A (NULL)";
-    case -8: return "invalid lda";
-    case -9: return "invalid B (NULL)";
-    case -10: return "invalid ldb";
-    case -11: return "invalid beta";
-    case -12: return "invalid C (NULL)";
-    case -13: return "invalid ldc";
-    case -14: return "invalid dtype";
-    case -15: return "invalid stream";
-    case -16: return "invalid splits";
-    case -17: return "invalid workspace (NULL or not 16-byte aligned)";
-    case -18: return "workspace too small";
+    case -1: return "invalid argument 1 (transA)";
+    case -2: return "invalid argument 2 (transB)";
+    case -3: return "invalid argument 3 (M)";
+    case -4: return "invalid argument 4 (N)";
+    case -5: return "invalid argument 5 (K)";
+    case -6: return "invalid argument 6 (alpha)";
+    case -7: return "invalid argument 7 (A is NULL)";
+    case -8: return "invalid argument 8 (lda)";
+    case -9: return "invalid argument 9 (B is NULL; dg_gemm_ex: strideA)";
+    case -10: return "invalid argument 10 (ldb; dg_gemm_ex: B is NULL)";
+    case -11: return "invalid argument 11 (beta; dg_gemm_ex: ldb)";
+    case -12: return "invalid argument 12 (C is NULL; dg_gemm_ex: strideB)";
+    case -13: return "invalid argument 13 (ldc; dg_gemm_ex: beta)";
+    case -14: return "invalid argument 14 (dtype; dg_gemm_ex: C is NULL)";
+    case -15: return "invalid argument 15 (stream; dg_gemm_ex: ldc)";
+    case -16: return "invalid argument 16 (dg_gemm_splitk: splits; dg_gemm_ex: strideC overlaps batches)";
+    case -17: return "invalid argument 17 (dg_gemm_splitk: workspace NULL or not 16-byte aligned; "
+                     "dg_gemm_ex: batch)";
+    case -18: return "invalid argument 18 (dg_gemm_splitk: workspace too small; dg_gemm_ex: bias "
+                     "not aligned to its element)";
+    case -19: return "invalid argument 19 (dg_gemm_ex: epilogue)";
+    case -20: return "invalid argument 20 (dg_gemm_ex: dtype)";
     default: return "unknown status";
     }
 }
 
 int dg_last_hip_error(void) { return g_last_hip_error; }
 
-int dg_version(void) { return 100; }
+int dg_version(void) { return 200; }
 
 }  // extern "C"

@@ -10,8 +10,13 @@ namespace dg {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Everything a kernel needs for one C = alpha*op(A)*op(B) + beta*C.
+// Epilogue activations (the values of dg_gemm_ex's `epilogue`).
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
+
+// Everything a kernel needs for one act(alpha*op(A)*op(B) + beta*C + bias),
+// or a strided batch of them.
 struct GemmParams {
     const void *A;
     const void *B;
@@ -28,12 +33,50 @@ struct GemmParams {
     int32_t splits;
     int32_t k_chunk;           // a multiple of every kernel's K slab
     float *ws;
+    // epilogue: bias[col] (N elements of C's type, NULL for none) is added
+    // after alpha and beta, then the activation `act` is applied
+    const void *bias;
+    int32_t act;
+    // strided batch: batch b (a grid dimension) uses A + b*strideA,
+    // B + b*strideB, C + b*strideC (elements); batch >= 1
+    int64_t strideA, strideB, strideC;
+    int32_t batch;
 };
 
 // A host-side launcher: enqueues one kernel on `stream`, returns a hipError_t.
 typedef hipError_t (*launch_fn)(const GemmParams &p, hipStream_t stream);
 
 #ifdef __HIPCC__
+// Point A, B and C at batch b.
+template <typename T>
+__device__ __forceinline__ void select_batch(GemmParams &p, int b)
+{
+    p.A = (const T *)p.A + (int64_t)b * p.strideA;
+    p.B = (const T *)p.B + (int64_t)b * p.strideB;
+    p.C = (T *)p.C + (int64_t)b * p.strideC;
+}
+
+// The activation of the epilogue, in fp32.  relu keeps NaN (the comparison
+// is false for it); gelu is x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)) with the
+// device erff.
+__device__ __forceinline__ float activate(int act, float x)
+{
+    if (act == ACT_RELU) return x < 0.f ? 0.f : x;
+    if (act == ACT_GELU) return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
+    return x;
+}
+
+// Everything after the accumulation for one output element: v = alpha*acc
+// (+ beta*c_in when beta != 0) + bias[col], then the activation, in fp32.
+template <typename T>
+__device__ __forceinline__ float epilogue_value(const GemmParams &p, float acc, float c_in, int col)
+{
+    float v = p.alpha * acc;
+    if (p.beta != 0.f) v = __builtin_fmaf(p.beta, c_in, v);
+    if (p.bias) v += (float)((const T *)p.bias)[col];
+    return activate(p.act, v);
+}
+
 // Workgroup id -> (split, id of the tile within the split) and the split's
 // k range [k_begin, k_begin + k_len).
 __device__ __forceinline__ void split_of(const GemmParams &p, int &bid, int &split, int &k_begin,

@@ -1,6 +1,7 @@
 // Matrix-core GEMM kernel template for gfx950 (CDNA4), 64-lane waves.
 //
-//   C[BM x BN tile] = alpha * sum_k op(A)[tile rows, k] op(B)[k, tile cols] + beta * C
+//   C[BM x BN tile] = act(alpha * sum_k op(A)[tile rows, k] op(B)[k, tile cols]
+//                         + beta * C + bias[cols]), batch blockIdx.y of a strided batch
 //
 // Hierarchy (the tiling of "Optimizing GEMM on Apple's M5 from scratch",
 // Part 1 Kernels 2-4 and Part 2 Kernels 6-7, recast for CDNA4):
@@ -183,6 +184,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
     constexpr int STAGE = OpA::ELEMS + OpB::ELEMS;
     __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
 
+    select_batch<T>(p, blockIdx.y);
     int bid, split, k_begin, Kl;
     split_of(p, bid, split, k_begin, Kl);
     // this split's k range starts at k_begin: offset the operands to it
@@ -308,9 +310,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
                     p.ws[((int64_t)split * p.M + row) * p.N + col] = acc[i][j][r];
                 } else if (row < p.M) {
                     T *c = C + (int64_t)row * p.ldc + col;
-                    float v = p.alpha * acc[i][j][r];
-                    if (p.beta != 0.f) v = __builtin_fmaf(p.beta, (float)*c, v);
-                    *c = (T)v;
+                    const float cin = p.beta != 0.f ? (float)*c : 0.f;
+                    *c = (T)epilogue_value<T>(p, acc[i][j][r], cin, col);
                 }
             }
         }
@@ -324,7 +325,7 @@ hipError_t launch_mfma(const GemmParams &p, hipStream_t s)
     GemmParams arg = p;
     void *args[] = {&arg};
     return hipLaunchKernel((const void *)&gemm_mfma_kernel<T, BM, BN, BK, WM, WN, TA, TB, VEC, MINW>,
-                           dim3(nwg), dim3(256), args, 0, s);
+                           dim3(nwg, p.batch), dim3(256), args, 0, s);
 }
 
 }  // namespace dg

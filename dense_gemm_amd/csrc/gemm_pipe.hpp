@@ -1,11 +1,15 @@
 // GEMM for gfx950 with a multi-stage LDS ring fed by direct global->LDS
-// loads, for fp16 operands (fp32 accumulation) and for fp32.
+// loads, for 16-bit operands (fp16 or bf16, fp32 accumulation) and for fp32.
 //
-//   C[BM x BN tile] = alpha * sum_k op(A)[rows, k] op(B)[k, cols] + beta * C,
-//   fp16: v_mfma_f32_32x32x16_f16 with fp32 accumulators ("Metal GEMM Kernels
-//   for LoRA Training on Apple Silicon", section 1: the fp32 accumulator keeps
-//   the fast path), K slabs of 64;
+//   C[BM x BN tile] = act(alpha * sum_k op(A)[rows, k] op(B)[k, cols]
+//                         + beta * C + bias[cols]),
+//   fp16 / bf16: v_mfma_f32_32x32x16_f16 / _bf16 with fp32 accumulators
+//   ("Metal GEMM Kernels for LoRA Training on Apple Silicon", section 1: the
+//   fp32 accumulator keeps the fast path), K slabs of 64;
 //   fp32: v_mfma_f32_32x32x2_f32, K slabs of 16.
+//   The bias and activation are the fused epilogue of "From a C loop to a GPU
+//   kernel", "Fusion"; grid y is the batch of a strided-batched call (the
+//   per-head offsets of "Metal GEMM Kernels for LoRA Training", section 8).
 //
 // Why a different kernel from gemm_mfma.hpp: at 2048^3 one 128 x 128 tile per
 // compute unit leaves a single wave per SIMD, and one 64-wide K slab is only
@@ -66,7 +70,6 @@ namespace dg {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
-typedef __attribute__((address_space(3))) f16x8 lds_f16x8_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int PIPE_BK = 64;
@@ -80,10 +83,12 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One fp16 operand of the pipelined kernel (K slab 64).
+// One 16-bit operand (fp16 or bf16) of the pipelined kernel (K slab 64).
 //   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
-template <int BMN, bool KCONT, int NW>
+template <typename E, int BMN, bool KCONT, int NW>
 struct PipeOperandH {
+    typedef E V8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) V8 lds_v8_t;
     static constexpr int BK = PIPE_BK;
     static constexpr int BYTES = BMN * PIPE_BK * 2;      // one stage
     static constexpr int LOADS = BYTES / (NW * 64 * 16);  // 16-byte loads per thread per slab
@@ -91,12 +96,12 @@ struct PipeOperandH {
     static constexpr int ROW_BYTES = KCONT ? PIPE_BK * 2 : BMN * 2;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide load fills
 
-    const _Float16 *ptr[LOADS];  // per-lane global addresses of the current slab
+    const E *ptr[LOADS];         // per-lane global addresses of the current slab
     int64_t step;                // elements to advance per slab
 
     // Per-lane addresses for the slab at k = 0.  mn0: first row (m or n) of
     // the tile; ext: M or N; ld: row stride of the stored matrix.
-    __device__ __forceinline__ void init(const _Float16 *g, int64_t ld, int mn0, int ext, int wave,
+    __device__ __forceinline__ void init(const E *g, int64_t ld, int mn0, int ext, int wave,
                                          int lane)
     {
 #pragma unroll
@@ -137,18 +142,18 @@ struct PipeOperandH {
                 const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
                 valid = r < krem ? 8 : 0;
             }
-            f16x8 v;
+            V8 v;
             if (valid >= 8) {
-                v = *(const f16x8 *)ptr[i];
+                v = *(const V8 *)ptr[i];
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    _Float16 x = (_Float16)0;
+                    E x = (E)0.f;
                     if (e < valid) x = ptr[i][e];
                     v[e] = x;
                 }
             }
-            *(lds_f16x8_t *)dst = v;
+            *(lds_v8_t *)dst = v;
             ptr[i] += step;
         }
     }
@@ -174,13 +179,13 @@ struct PipeOperandH {
     }
 
     // MFMA operand of block rows [b0, b0+32) for k-step kk (16 k) of a stage.
-    __device__ __forceinline__ f16x8 frag(const lds_char_t *lds, int b0, int kk, int lane) const
+    __device__ __forceinline__ V8 frag(const lds_char_t *lds, int b0, int kk, int lane) const
     {
         if constexpr (KCONT) {
             const int r = b0 + (lane & 31);
             const int c = 2 * kk + (lane >> 5);
             const int p = c ^ ((r >> 1) & 7);
-            return *(const lds_f16x8_t *)(lds + r * ROW_BYTES + p * 16);
+            return *(const lds_v8_t *)(lds + r * ROW_BYTES + p * 16);
         } else {
             const int g = lane >> 4, j = lane & 15, t = j >> 2, s = j & 3;
             const int q = b0 >> 5;
@@ -192,7 +197,7 @@ struct PipeOperandH {
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
             typedef short i16x8 __attribute__((ext_vector_type(8)));
             const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            return __builtin_bit_cast(f16x8, v);
+            return __builtin_bit_cast(V8, v);
         }
     }
 };
@@ -304,6 +309,16 @@ struct PipeOperandS {
     }
 };
 
+// The 32x32x16 matrix-core step for either 16-bit operand type (fp32 accumulators).
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // Waves: (BM/WM) x (BN/WN) sub-tiles per K group, KSPLIT groups.  Group g
 // runs the 16-k steps [g*4/KSPLIT, (g+1)*4/KSPLIT) of every slab, so with a
 // 128 x 128 tile of 64 x 64 sub-tiles and KSPLIT = 2 each SIMD holds two
@@ -316,7 +331,8 @@ struct PipeOperandS {
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_pipe_kernel(GemmParams p)
 {
-    constexpr bool F16 = sizeof(T) == 2;
+    constexpr bool HALF = sizeof(T) == 2;          // fp16 or bf16 operands
+    typedef T V8 __attribute__((ext_vector_type(8)));
     constexpr int WAVES_N = BN / WN;
     constexpr int NWG = (BM / WM) * WAVES_N;       // waves per K group
     constexpr int NW = NWG * KSPLIT;               // waves per workgroup
@@ -326,9 +342,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     constexpr int KPW = (PIPE_BK / 16) / KSPLIT;   // fp16: 16-k steps per wave per slab
     static_assert(KPW >= 1 && KPW * KSPLIT == PIPE_BK / 16, "K split");
     static_assert(KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
-    static_assert(F16 || KSPLIT == 1, "fp32 runs without K groups");
-    typedef typename std::conditional<F16, PipeOperandH<BM, !TA, NW>, PipeOperandS<BM, !TA, NW>>::type OpA;
-    typedef typename std::conditional<F16, PipeOperandH<BN, TB, NW>, PipeOperandS<BN, TB, NW>>::type OpB;
+    static_assert(HALF || KSPLIT == 1, "fp32 runs without K groups");
+    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW>, PipeOperandS<BM, !TA, NW>>::type OpA;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW>, PipeOperandS<BN, TB, NW>>::type OpB;
     constexpr int BK = OpA::BK;
     constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
     constexpr int SMEM = STAGES * STAGE_BYTES;
@@ -348,6 +364,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     const int wm0 = (wq / WAVES_N) * WM;
     const int wn0 = (wq % WAVES_N) * WN;
     const int kk0 = kgroup * KPW;
+    select_batch<T>(p, blockIdx.y);
     int bid, split, k_begin, Kl;
     split_of(p, bid, split, k_begin, Kl);
     int tm, tn;
@@ -376,7 +393,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     };
     // fp16 keeps STAGES slabs in flight, fp32 STAGES - 1 (see the loops below)
 #pragma unroll
-    for (int s = 0; s < (F16 ? STAGES : STAGES - 1); ++s) {
+    for (int s = 0; s < (HALF ? STAGES : STAGES - 1); ++s) {
         if (s < nk) issue_slab(s, smem + s * STAGE_BYTES);
     }
 
@@ -390,14 +407,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 acc[i][j][r] = 0.f;
 
     constexpr int LOADS = OpA::LOADS + OpB::LOADS;
-    if constexpr (F16) {
+    if constexpr (HALF) {
         // Two fragment sets, the loop unrolled by two so that each set stays
         // in fixed registers.  The next slab's LDS reads are unconditional:
         // after the last slab they read a stale stage that is never used, so
         // that no branch separates them from the MFMAs (the compiler's LDS
         // wait bookkeeping would otherwise wait for them before the MFMAs).
-        f16x8 fa0[KPW][TM], fb0[KPW][TN], fa1[KPW][TM], fb1[KPW][TN];
-        auto read = [&](int slab, f16x8(&fa)[KPW][TM], f16x8(&fb)[KPW][TN]) {
+        V8 fa0[KPW][TM], fb0[KPW][TN], fa1[KPW][TM], fb1[KPW][TN];
+        auto read = [&](int slab, V8(&fa)[KPW][TM], V8(&fb)[KPW][TN]) {
             const lds_char_t *sA = smem + (slab % STAGES) * STAGE_BYTES;
             const lds_char_t *sB = sA + OpA::BYTES;
 #pragma unroll
@@ -408,8 +425,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 for (int j = 0; j < TN; ++j) fb[s][j] = gb.frag(sB, wn0 + 32 * j, kk0 + s, lane);
             }
         };
-        auto step = [&](int kt, f16x8(&ca)[KPW][TM], f16x8(&cb)[KPW][TN], f16x8(&na)[KPW][TM],
-                        f16x8(&nb)[KPW][TN]) {
+        auto step = [&](int kt, V8(&ca)[KPW][TM], V8(&cb)[KPW][TN], V8(&na)[KPW][TM],
+                        V8(&nb)[KPW][TN]) {
             // slabs issued so far: [0, min(nk, kt + STAGES)); slab kt+1 must be complete
             if (kt + STAGES <= nk) wait_vmcnt<(STAGES - 2) * LOADS>();
             else wait_vmcnt<0>();
@@ -422,7 +439,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ca[s][i], cb[s][j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = mfma_32x32x16(ca[s][i], cb[s][j], acc[i][j]);
         };
         if (nk > 0) {
             if (nk >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
@@ -516,9 +533,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     // Accumulator register r of lane l in a 32x32 block holds row
     // 8*(r/4) + 4*(l/32) + r%4, column l%32.  Each owned block is staged in
     // this wave's LDS slot as fp32 [32][EPI_LD]; lane l then takes row l/2,
-    // columns 16*(l%2) .. +15, and writes them with two 16-byte stores (one
-    // rounding to fp16 per element), or element by element at the matrix
-    // edge or when C rows are not 16-byte aligned.
+    // columns 16*(l%2) .. +15, forms alpha*acc + beta*C + bias and the
+    // activation in fp32, and writes them with 16-byte stores (one rounding to
+    // the output type per element), or element by element at the matrix edge
+    // or when C rows are not 16-byte aligned.
     T *C = (T *)p.C;
     lds_char_t *stg = smem + wave * 32 * EPI_LD * 4;
     typedef __attribute__((address_space(3))) float lds_float_t;
@@ -561,46 +579,51 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             }
             continue;
         }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] *= p.alpha;
+        // alpha, beta, bias and the activation in fp32, one rounding to T
         T *c = C + (int64_t)grow * p.ldc + gcol;
         if (p.c_vec && grow < p.M && gcol + 16 <= p.N) {
-            if constexpr (F16) {
-                if (p.beta != 0.f) {
-                    const f16x8 c0 = *(const f16x8 *)c, c1 = *(const f16x8 *)(c + 8);
+            float cin[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) cin[e] = 0.f;
+            if (p.beta != 0.f) {
+                if constexpr (HALF) {
+                    const V8 c0 = *(const V8 *)c, c1 = *(const V8 *)(c + 8);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        v[e] = __builtin_fmaf(p.beta, (float)c0[e], v[e]);
-                        v[8 + e] = __builtin_fmaf(p.beta, (float)c1[e], v[8 + e]);
+                        cin[e] = (float)c0[e];
+                        cin[8 + e] = (float)c1[e];
                     }
-                }
-                f16x8 o0, o1;
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    o0[e] = (_Float16)v[e];
-                    o1[e] = (_Float16)v[8 + e];
-                }
-                *(f16x8 *)c = o0;
-                *(f16x8 *)(c + 8) = o1;
-            } else {
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    f32x4 o = {v[4 * c4], v[4 * c4 + 1], v[4 * c4 + 2], v[4 * c4 + 3]};
-                    if (p.beta != 0.f) {
+                    for (int c4 = 0; c4 < 4; ++c4) {
                         const f32x4 ci = *(const f32x4 *)(c + 4 * c4);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(p.beta, ci[e], o[e]);
+                        for (int e = 0; e < 4; ++e) cin[4 * c4 + e] = ci[e];
                     }
-                    *(f32x4 *)(c + 4 * c4) = o;
                 }
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = epilogue_value<T>(p, v[e], cin[e], gcol + e);
+            if constexpr (HALF) {
+                V8 o0, o1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o0[e] = (T)v[e];
+                    o1[e] = (T)v[8 + e];
+                }
+                *(V8 *)c = o0;
+                *(V8 *)(c + 8) = o1;
+            } else {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    *(f32x4 *)(c + 4 * c4) = (f32x4){v[4 * c4], v[4 * c4 + 1], v[4 * c4 + 2], v[4 * c4 + 3]};
             }
         } else if (grow < p.M) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 if (gcol + e < p.N) {
-                    float x = v[e];
-                    if (p.beta != 0.f) x = __builtin_fmaf(p.beta, (float)c[e], x);
-                    c[e] = (T)x;
+                    const float cin = p.beta != 0.f ? (float)c[e] : 0.f;
+                    c[e] = (T)epilogue_value<T>(p, v[e], cin, gcol + e);
                 }
             }
         }
@@ -614,7 +637,7 @@ hipError_t launch_pipe(const GemmParams &p, hipStream_t s)
     GemmParams arg = p;
     void *args[] = {&arg};
     return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT>,
-                           dim3(nwg), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
+                           dim3(nwg, p.batch), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
 }
 
 }  // namespace dg

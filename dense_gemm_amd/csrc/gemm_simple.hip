@@ -1,5 +1,6 @@
 // Generic GEMM kernel: any shape, any leading dimension, any alignment, all
-// four transpose pairs, fp32 or fp16 operands, fp32 accumulation.
+// four transpose pairs, fp32, fp16 or bf16 operands, fp32 accumulation, the
+// bias + activation epilogue and strided batches (grid z).
 //
 // Structure: the shared-memory tiling of "Optimizing GEMM on Apple's M5 from
 // scratch, Part 1" (Kernels 2 and 3: stage a tile of each operand on chip,
@@ -10,8 +11,9 @@
 // its own, so no alignment is assumed; lanes run along whichever dimension
 // the stored matrix has contiguous.
 //
-// This is the fallback for problems the matrix-core kernels do not take, and
-// it also serves the C = beta*C case (alpha == 0 or K == 0).
+// This is the fallback for problems the matrix-core kernels do not take; the
+// other kernels here serve the case without a product (alpha == 0 or K == 0)
+// and the split-K reduction.
 #include "gemm_common.hpp"
 
 namespace dg {
@@ -30,6 +32,7 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(GemmParams p)
 {
     __shared__ float As[SK][ST + SPAD];
     __shared__ float Bs[SK][ST + SPAD];
+    select_batch<T>(p, blockIdx.z);
     const T *A = (const T *)p.A;
     const T *B = (const T *)p.B;
     T *C = (T *)p.C;
@@ -94,24 +97,27 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(GemmParams p)
             const int gn = n0 + tx * 4 + j;
             if (gn >= p.N) continue;
             T *c = C + (int64_t)gm * p.ldc + gn;
-            float v = p.alpha * acc[i][j];
-            if (p.beta != 0.f) v = __builtin_fmaf(p.beta, to_f32(*c), v);
-            *c = (T)v;
+            const float cin = p.beta != 0.f ? to_f32(*c) : 0.f;
+            *c = (T)epilogue_value<T>(p, acc[i][j], cin, gn);
         }
     }
 }
 
-// C = beta * C over the M x N view (beta == 0 writes zeros without reading C).
+// No product term (alpha == 0 or K == 0): C = act(beta * C + bias) over the
+// M x N view of batch blockIdx.y; beta == 0 does not read C.
 template <typename T>
 __global__ __launch_bounds__(256) void scale_c_kernel(GemmParams p)
 {
+    select_batch<T>(p, blockIdx.y);
     T *C = (T *)p.C;
     const int64_t total = (int64_t)p.M * p.N;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * 256) {
         const int64_t i = e / p.N, j = e - i * p.N;
         T *c = C + i * p.ldc + j;
-        *c = (p.beta == 0.f) ? (T)0.f : (T)(p.beta * to_f32(*c));
+        float v = p.beta != 0.f ? p.beta * to_f32(*c) : 0.f;
+        if (p.bias) v += to_f32(((const T *)p.bias)[j]);
+        *c = (T)activate(p.act, v);
     }
 }
 
@@ -146,9 +152,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p)
             if (e < mn) {
                 const int64_t i = e / p.N, j = e - i * p.N;
                 T *c = C + i * p.ldc + j;
-                float v = p.alpha * acc[u];
-                if (p.beta != 0.f) v = __builtin_fmaf(p.beta, to_f32(*c), v);
-                *c = (T)v;
+                const float cin = p.beta != 0.f ? to_f32(*c) : 0.f;
+                *c = (T)epilogue_value<T>(p, acc[u], cin, (int)j);
             }
         }
     }
@@ -169,7 +174,7 @@ hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t s)
 template <typename T, bool TA, bool TB>
 hipError_t launch_simple(const GemmParams &p, hipStream_t s)
 {
-    dim3 grid((p.N + ST - 1) / ST, (p.M + ST - 1) / ST);
+    dim3 grid((p.N + ST - 1) / ST, (p.M + ST - 1) / ST, p.batch);
     GemmParams arg = p;
     void *args[] = {&arg};
     return hipLaunchKernel((const void *)&gemm_simple_kernel<T, TA, TB>, grid, dim3(256), args, 0, s);
@@ -180,11 +185,11 @@ hipError_t launch_scale(const GemmParams &p, hipStream_t s)
 {
     const int64_t total = (int64_t)p.M * p.N;
     int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
+    if (blocks > 8192) blocks = 8192;
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&scale_c_kernel<T>, dim3((unsigned)blocks), dim3(256), args,
-                           0, s);
+    return hipLaunchKernel((const void *)&scale_c_kernel<T>, dim3((unsigned)blocks, p.batch), dim3(256),
+                           args, 0, s);
 }
 
 }  // namespace
@@ -192,23 +197,28 @@ hipError_t launch_scale(const GemmParams &p, hipStream_t s)
 // launchers exported to the dispatcher: [dtype][transA][transB]
 launch_fn simple_launcher(int dtype, int ta, int tb)
 {
-    static const launch_fn table[2][2][2] = {
+    static const launch_fn table[3][2][2] = {
         {{launch_simple<float, false, false>, launch_simple<float, false, true>},
          {launch_simple<float, true, false>, launch_simple<float, true, true>}},
         {{launch_simple<_Float16, false, false>, launch_simple<_Float16, false, true>},
          {launch_simple<_Float16, true, false>, launch_simple<_Float16, true, true>}},
+        {{launch_simple<__bf16, false, false>, launch_simple<__bf16, false, true>},
+         {launch_simple<__bf16, true, false>, launch_simple<__bf16, true, true>}},
     };
     return table[dtype][ta][tb];
 }
 
 launch_fn splitk_reduce_launcher(int dtype)
 {
-    return dtype == 0 ? launch_splitk_reduce<float> : launch_splitk_reduce<_Float16>;
+    static const launch_fn table[3] = {launch_splitk_reduce<float>, launch_splitk_reduce<_Float16>,
+                                       launch_splitk_reduce<__bf16>};
+    return table[dtype];
 }
 
 launch_fn scale_launcher(int dtype)
 {
-    return dtype == 0 ? launch_scale<float> : launch_scale<_Float16>;
+    static const launch_fn table[3] = {launch_scale<float>, launch_scale<_Float16>, launch_scale<__bf16>};
+    return table[dtype];
 }
 
 }  // namespace dg

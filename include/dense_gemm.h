@@ -25,15 +25,20 @@
  * read and never written.
  *
  * Types (dtype):
- *   DG_F32        A, B, C are fp32; products and sums in fp32 on the fp32
- *                 matrix cores (full precision, no reduced-precision inputs).
- *   DG_F16_F32ACC A, B, C are IEEE fp16; products are accumulated in fp32
- *                 (the fp16 matrix-core path with fp32 accumulators -- "Metal
- *                 GEMM Kernels for LoRA Training", section 1); the result
- *                 alpha*acc + beta*C is formed in fp32 (an fp16 C is widened
- *                 exactly) and rounded once to fp16, round-to-nearest-even,
- *                 overflow to +-Inf.
- *   alpha and beta are fp32 for both types.
+ *   DG_F32         A, B, C are fp32; products and sums in fp32 on the fp32
+ *                  matrix cores (full precision, no reduced-precision inputs).
+ *   DG_F16_F32ACC  A, B, C are IEEE fp16; products are accumulated in fp32
+ *                  (the fp16 matrix-core path with fp32 accumulators -- "Metal
+ *                  GEMM Kernels for LoRA Training", section 1); the result
+ *                  alpha*acc + beta*C is formed in fp32 (an fp16 C is widened
+ *                  exactly) and rounded once to fp16, round-to-nearest-even,
+ *                  overflow to +-Inf.
+ *   DG_BF16_F32ACC A, B, C are bfloat16 (8 significant bits, fp32's exponent
+ *                  range); as DG_F16_F32ACC otherwise: fp32 accumulation, one
+ *                  round-to-nearest-even to bf16 at the end.  The page above
+ *                  (section 1) has bf16 emulated on its GPU; gfx950 has a
+ *                  native bf16 matrix-core instruction.
+ *   alpha and beta are fp32 for every type.
  *
  * Special values of the arguments:
  *   M == 0 or N == 0       nothing is done (returns DG_OK).
@@ -71,7 +76,9 @@ extern "C" {
 #endif
 
 enum { DG_OP_N = 0, DG_OP_T = 1 };
-enum { DG_F32 = 0, DG_F16_F32ACC = 1 };
+enum { DG_F32 = 0, DG_F16_F32ACC = 1, DG_BF16_F32ACC = 2 };
+/* Epilogue activations of dg_gemm_ex. */
+enum { DG_EPI_NONE = 0, DG_EPI_RELU = 1, DG_EPI_GELU = 2 };
 
 #define DG_OK 0
 #define DG_ERR_UNSUPPORTED (-100)
@@ -93,6 +100,52 @@ int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha
 int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
                         void *C, int64_t ldc, int dtype, void *stream, int kernel);
+
+/* Extended form: a fused bias + activation epilogue and strided batches.
+ *
+ *   for b in 0 .. batch-1:
+ *     C_b = act(alpha * op(A_b) * op(B_b) + beta * C_b + bias)
+ *     with A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC
+ *     (strides in elements).
+ *
+ * The epilogue is the fusion of "From a C loop to a GPU kernel", section
+ * "Fusion": a per-output bias is added and an elementwise activation applied
+ * while the tile is still on chip, and the result is written once.  In a
+ * row-major C the outputs of one feature are a column, so bias[j] is added to
+ * every element of column j:
+ *   x = alpha*acc + beta*C_in + bias[j]   (in fp32, one rounding at the end)
+ *   epilogue DG_EPI_NONE: x;  DG_EPI_RELU: max(x, 0) (NaN stays NaN);
+ *   DG_EPI_GELU: x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))), the exact-erf
+ *   form, Phi the standard normal distribution function.
+ * The batch is the per-head offset of "Metal GEMM Kernels for LoRA Training",
+ * section 8 (Q, K, V head-major, one GEMM per head at a fixed offset): one
+ * call runs every head, so the heads together fill the GPU.
+ *
+ * Arguments (1-based positions, for the -i error codes):
+ *   1-8, 10-11, 13-15, 20-21: as dg_gemm's transA, transB, M, N, K, alpha,
+ *       A, lda, B, ldb, beta, C, ldc, dtype, stream.
+ *   9 strideA, 12 strideB: >= 0 (0 reuses one matrix for every batch).
+ *   16 strideC: >= 0; with batch > 1 the outputs must not overlap:
+ *       strideC >= (M-1)*ldc + N.
+ *   17 batch: 0 .. 65535 (0: nothing is done).
+ *   18 bias: NULL (no bias) or N elements of C's type, contiguous, aligned
+ *       to its element size, shared by every batch; caller-owned device
+ *       memory.
+ *   19 epilogue: DG_EPI_NONE, DG_EPI_RELU or DG_EPI_GELU.
+ * Special values as dg_gemm; with K == 0 or alpha == 0 the result is
+ * act(beta*C + bias) and A and B are not read.  Pointer rules, asynchrony and
+ * errors as dg_gemm (nothing enqueued on error).  No allocation. */
+int dg_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+               const void *A, int64_t lda, int64_t strideA, const void *B, int64_t ldb,
+               int64_t strideB, float beta, void *C, int64_t ldc, int64_t strideC,
+               int64_t batch, const void *bias, int epilogue, int dtype, void *stream);
+
+/* dg_gemm_ex with a forced kernel, as dg_gemm_with_kernel (argument 22). */
+int dg_gemm_ex_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                           const void *A, int64_t lda, int64_t strideA, const void *B,
+                           int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc,
+                           int64_t strideC, int64_t batch, const void *bias, int epilogue,
+                           int dtype, void *stream, int kernel);
 
 /* Split-K form of dg_gemm, for outputs too small to give every compute unit a
  * tile (skinny and low-rank products): K is cut into `splits` ranges (each a

@@ -58,7 +58,7 @@ def call(**kw):
     (dict(M=-1), -3), (dict(N=-5), -4), (dict(K=-1), -5), (dict(M=2 ** 31), -3),
     (dict(A=NULL), -7), (dict(lda=15), -8), (dict(ta=1, lda=15), -8),
     (dict(B=NULL), -9), (dict(ldb=15), -10), (dict(tb=1, ldb=15), -10),
-    (dict(C=NULL), -12), (dict(ldc=15), -13), (dict(dtype=2), -14), (dict(dtype=-1), -14),
+    (dict(C=NULL), -12), (dict(ldc=15), -13), (dict(dtype=3), -14), (dict(dtype=-1), -14),
     # the first invalid argument is the one reported
     (dict(ta=9, M=-1, dtype=5), -1), (dict(lda=1, ldc=1), -8),
 ])
@@ -93,7 +93,7 @@ def test_kernel_table():
     assert n == len(names) >= 4
     assert len(set(names)) == n
     for i, name in enumerate(names):
-        assert name.split("_")[0] in ("f32", "f16")
+        assert name.split("_")[0] in ("f32", "f16", "bf16")
         bm, bn = dg.dg_kernel_tile_m(i), dg.dg_kernel_tile_n(i)
         assert f"{bm}x{bn}" in name
     assert dg.dg_kernel_name(n) is None and dg.dg_kernel_name(-1) is None
@@ -109,12 +109,16 @@ def test_forced_kernel_out_of_range_is_unsupported():
 
 
 def test_selection_picks_matrix_core_kernels_of_the_right_type():
-    for dtype, prefix in ((0, "f32_"), (1, "f16_")):
+    for dtype, prefix in ((0, "f32_"), (1, "f16_"), (2, "bf16_")):
         for M, N, K in ((4096, 4096, 4096), (2048, 2048, 2048), (512, 32, 5632), (1, 1, 1),
                         (8192, 256, 8192), (4095, 4097, 1031)):
             k = dg.dg_select_kernel(0, 0, M, N, K, NULL, K, NULL, N, NULL, N, dtype)
             name = dg.dg_kernel_name(k)
-            assert name.startswith(prefix) and "mfma" in name, (M, N, K, name)
+            assert name.startswith(prefix), (M, N, K, name)
+            # bf16 has only the pipelined matrix-core kernels; rows that are not
+            # whole 16-byte pieces fall back to the generic kernel
+            aligned = K % 8 == 0 and N % 8 == 0
+            assert ("mfma" in name) == (dtype != 2 or aligned), (M, N, K, name)
     # the headline shapes get the large tiles
     k = dg.dg_select_kernel(0, 0, 4096, 4096, 4096, NULL, 4096, NULL, 4096, NULL, 4096, 0)
     assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 128)
@@ -169,4 +173,70 @@ def test_splitk_invalid_arguments():
     # a workspace too small for the ranges used: rejected before any launch
     assert sk(M=512, N=32, K=5632, lda=5632, ldb=32, ldc=32, splits=8, wsb=1024) == -18
     assert sk(M=0, ws=None) == 0                # empty output: nothing to do
-    assert dg.dg_status_string(-18) == "workspace too small"
+    assert "workspace too small" in dg.dg_status_string(-18)
+
+
+# ---- the extended entry point (bias + activation epilogue, strided batches) ----
+GOOD_EX = dict(ta=0, tb=0, M=16, N=16, K=16, alpha=1.0, A=0x1000, lda=16, sA=256, B=0x2000, ldb=16,
+               sB=256, beta=0.0, C=0x3000, ldc=16, sC=256, batch=2, bias=0x4000, epi=1, dtype=1,
+               stream=NULL)
+
+
+def call_ex(**kw):
+    a = dict(GOOD_EX)
+    a.update(kw)
+    return dg.dg_gemm_ex(a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"],
+                         a["sA"], a["B"], a["ldb"], a["sB"], a["beta"], a["C"], a["ldc"], a["sC"],
+                         a["batch"], a["bias"], a["epi"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ta=2), -1), (dict(tb=-1), -2), (dict(M=-1), -3), (dict(N=-1), -4), (dict(K=-1), -5),
+    (dict(A=NULL), -7), (dict(lda=15), -8), (dict(sA=-1), -9),
+    (dict(B=NULL), -10), (dict(ldb=15), -11), (dict(sB=-16), -12),
+    (dict(C=NULL), -14), (dict(ldc=15), -15),
+    # batches of C overlap: batch 1 would start inside batch 0 (needs >= 15*16+16)
+    (dict(sC=-1), -16), (dict(sC=255), -16), (dict(ldc=32, sC=256 + 16), -16),
+    (dict(batch=-1), -17), (dict(batch=65536), -17),
+    (dict(bias=0x4001), -18),            # fp16 bias not aligned to its element
+    (dict(epi=3), -19), (dict(epi=-1), -19),
+    (dict(dtype=3), -20),
+    (dict(ta=9, sA=-1, epi=7), -1),      # the first invalid argument is the one reported
+])
+def test_ex_invalid_arguments(kw, code):
+    assert call_ex(**kw) == code
+    assert dg.dg_status_string(code).startswith("invalid")
+
+
+def test_ex_quick_returns_and_valid_strides():
+    assert call_ex(M=0) == 0
+    assert call_ex(batch=0, A=NULL, B=NULL, C=NULL) == 0      # nothing to do, nothing read
+    assert call_ex(M=0, C=NULL, batch=3) == 0
+    # the tightest non-overlapping C stride, and stride 0 for a shared A or B, pass the checks:
+    # M = 0 keeps the call on the CPU
+    assert call_ex(M=0, sC=0, batch=1) == 0
+    assert call_ex(M=0, sA=0, sB=0) == 0
+    # fp32 bias needs 4-byte alignment
+    assert call_ex(dtype=0, bias=0x4002) == -18
+    assert call_ex(dtype=0, bias=0x4004, M=0) == 0
+
+
+def test_ex_forced_kernel_checks():
+    n = dg.dg_kernel_count()
+    a = dict(GOOD_EX)
+    rc = dg.dg_gemm_ex_with_kernel(0, 0, 16, 16, 16, 1.0, 0x1000, 16, 256, 0x2000, 16, 256, 0.0,
+                                   0x3000, 16, 256, 2, NULL, 0, 1, NULL, n)
+    assert rc == dg.DG_ERR_UNSUPPORTED
+    # a kernel of another dtype is refused before any launch
+    f32_kernel = dg.kernel_names().index("f32_64x64_simple")
+    rc = dg.dg_gemm_ex_with_kernel(0, 0, 16, 16, 16, 1.0, 0x1000, 16, 256, 0x2000, 16, 256, 0.0,
+                                   0x3000, 16, 256, 2, NULL, 0, 1, NULL, f32_kernel)
+    assert rc == dg.DG_ERR_UNSUPPORTED
+    del a
+
+
+def test_bf16_kernels_listed():
+    names = dg.kernel_names()
+    for n in ("bf16_64x64_simple", "bf16_128x128_pipe4_ksplit2_mfma32x32x16",
+              "bf16_256x128_pipe2_w8_mfma32x32x16"):
+        assert n in names

@@ -29,8 +29,7 @@ def dg():
 
 
 def kernels_for(dg, dtype):
-    prefix = "f32_" if dtype == "f32" else "f16_"
-    return [i for i, n in enumerate(dg.kernel_names()) if n.startswith(prefix)]
+    return [i for i, n in enumerate(dg.kernel_names()) if n.startswith(dtype + "_")]
 
 
 def pipe_ok(p):
@@ -57,7 +56,7 @@ def run_or_unsupported(dg, p, k, **kw):
 # ---------------------------------------------------------------------------
 # every kernel x transpose pair x alignment, ragged shapes over several tiles
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("ta,tb", TRANS)
 @pytest.mark.parametrize("aligned", [True, False])
 def test_every_kernel_ragged(dg, dtype, ta, tb, aligned):
@@ -77,7 +76,7 @@ def test_every_kernel_ragged(dg, dtype, ta, tb, aligned):
             check_full(p, kernel=k, out=out)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("dtype", ["f16", "f32", "bf16"])
 @pytest.mark.parametrize("ta,tb", TRANS)
 @pytest.mark.parametrize("shape", [(296, 264, 192), (1000, 1032, 512), (136, 8, 64), (8, 136, 128),
                                    (264, 520, 256), (264, 136, 32), (136, 264, 100), (200, 144, 1),
@@ -101,7 +100,7 @@ def test_pipelined_kernels(dg, dtype, ta, tb, shape):
             check_full(p, kernel=k)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_unaligned_pointers(dg, dtype):
     M, N, K = 129, 257, 77
     a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 120, with_c0=True)
@@ -116,7 +115,7 @@ def test_unaligned_pointers(dg, dtype):
 # ---------------------------------------------------------------------------
 # brute force over every tiny shape
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_all_tiny_shapes(dg, dtype):
     for M, N, K in itertools.product(range(1, 9), repeat=3):
         a, b, c0 = synth.problem(M, N, K, dtype, "uniform", M * 100 + N * 10 + K, with_c0=True)
@@ -159,7 +158,8 @@ def test_f16_output_rounding_is_rne_and_overflows_to_inf(dg):
             out = p.run_gpu()[:, :N]
             with np.errstate(over="ignore"):
                 want = (alpha * exact.astype(np.float64)).astype(np.float16)
-            assert np.array_equal(out.view(np.uint16), want.view(np.uint16)), (alpha, ta, tb)
+            got = np.ascontiguousarray(out).astype(np.float16)    # exact: fp16 values
+            assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), (alpha, ta, tb)
         if alpha == 4.0:
             assert np.isinf(want).any() and np.isfinite(want).any()
 
@@ -167,7 +167,7 @@ def test_f16_output_rounding_is_rne_and_overflows_to_inf(dg):
 # ---------------------------------------------------------------------------
 # alpha / beta / empty cases and what the library does not touch
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_beta_zero_ignores_nan_in_C(dg, dtype):
     a, b, _ = synth.problem(70, 90, 33, dtype, "uniform", 150)
     p = Problem(a, b, None, False, True, 1.0, 0.0, dtype, (4, 4, 4))  # C holds NaN
@@ -313,7 +313,7 @@ def test_splitk(dg, dtype, ta, tb, shape, splits):
     p = Problem(a, b, c0, ta, tb, -1.25, 0.5, dtype, pad)
     out = run_splitk(dg, p, splits)
     p.check_padding(out)
-    ref, ab = p.oracle_full()
+    ref, ab, _ = p.oracle_full()
     worst, bad = oracle.compare(dtype, out[:, :N].astype(np.float64), ref, ab, p.alpha, p.beta, c0)
     assert bad == 0, f"{bad} elements out of bound, max err/bound {worst:.3g}"
 
@@ -324,7 +324,7 @@ def test_lora_skinny_splitk(dg, index):
     a, b, c0 = synth.lora_problem(index, seed=3)
     p = Problem(a, b, c0, ta, tb, 1.0, beta, "f16")
     out = run_splitk(dg, p, 0)
-    ref, ab = p.oracle_full()
+    ref, ab, _ = p.oracle_full()
     worst, bad = oracle.compare("f16", out[:, :N].astype(np.float64), ref, ab, 1.0, beta, c0)
     assert bad == 0, f"{name}: {bad} elements out of bound, max err/bound {worst:.3g}"
 
