@@ -131,6 +131,123 @@ def lora_step(dev, stream, reps):
             "tokens_per_s": round(512 / t_step, 1), "per_gemm": per}
 
 
+def _dev_tensor(x, dtype, dev):
+    """A host array of the given storage type as a device tensor (bf16 from
+    its uint16 bit patterns)."""
+    import numpy as np
+    import torch
+    x = np.ascontiguousarray(x)
+    if dtype == "bf16":
+        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(x).to(dev)
+
+
+def bf16_square(dev, stream, reps):
+    """bf16 operands, fp32 accumulation, bf16 output at 2048^3, nn/tn/nt, with
+    the fp16 workload's recipe (N(0,1)/sqrt(K), seed 2)."""
+    import torch
+
+    import dense_gemm_amd as dg
+    import synth
+    S = 2048
+    a, b, _ = synth.problem(S, S, S, "bf16", "normal_sqrtk", 2)
+    res = {"peak": PEAK_F16, "unit": "TFLOP/s"}
+    for name, ta, tb in (("nn", 0, 0), ("tn", 1, 0), ("nt", 0, 1)):
+        A = _dev_tensor(a.T if ta else a, "bf16", dev)
+        B = _dev_tensor(b.T if tb else b, "bf16", dev)
+        C = torch.empty((S, S), dtype=torch.bfloat16, device=dev)
+        k = dg.dg_select_kernel(ta, tb, S, S, S, A.data_ptr(), S, B.data_ptr(), S, C.data_ptr(), S,
+                                dg.DG_BF16_F32ACC)
+
+        def f(ta=ta, tb=tb, A=A, B=B, C=C):
+            rc = dg.dg_gemm(ta, tb, S, S, S, 1.0, A.data_ptr(), S, B.data_ptr(), S, 0.0,
+                            C.data_ptr(), S, dg.DG_BF16_F32ACC, stream.cuda_stream)
+            if rc != 0:
+                raise dg.GemmError(rc)
+
+        for _ in range(20):
+            f()
+        torch.cuda.synchronize()
+        t = min(time_launches(f, stream, reps) for _ in range(3))
+        ach = tflops(S, S, S, t)
+        res[name] = {"tflops": round(ach, 2), "frac": round(ach / PEAK_F16, 4),
+                     "kernel_us": round(t * 1e6, 2), "kernel": dg.dg_kernel_name(k)}
+    return res
+
+
+def attention_heads(dev, stream, reps):
+    """The six per-head products of attention (head-major Q, K, V; "Metal GEMM
+    Kernels for LoRA Training", section 8) for 512 tokens and 32 heads of 64,
+    fp16, each one strided-batched call over the heads."""
+    import torch
+
+    import dense_gemm_amd as dg
+    import synth
+    T, D, H = 512, 64, 32
+    products = [("S = Q K^T", T, T, D, 0, 1), ("O = P V", T, D, T, 0, 0),
+                ("dV = P^T dO", T, D, T, 1, 0), ("dP = dO V^T", T, T, D, 0, 1),
+                ("dQ = dS K", T, D, T, 0, 0), ("dK = dS^T Q", T, D, T, 1, 0)]
+    st = synth.Stream(40)
+    per, total_t, total_f = [], 0.0, 0.0
+    for name, M, N, K, ta, tb in products:
+        sa, sb = M * K, K * N
+        A = _dev_tensor(synth.round_to(st.normal((H * sa,)), "f16"), "f16", dev)
+        B = _dev_tensor(synth.round_to(st.normal((H * sb,)) / K ** 0.5, "f16"), "f16", dev)
+        C = torch.empty((H, M, N), dtype=torch.float16, device=dev)
+        lda, ldb = (M if ta else K), (K if tb else N)
+
+        def f(M=M, N=N, K=K, ta=ta, tb=tb, A=A, B=B, C=C, lda=lda, ldb=ldb, sa=sa, sb=sb):
+            rc = dg.dg_gemm_ex(ta, tb, M, N, K, 1.0, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
+                               0.0, C.data_ptr(), N, M * N, H, None, dg.DG_EPI_NONE,
+                               dg.DG_F16_F32ACC, stream.cuda_stream)
+            if rc != 0:
+                raise dg.GemmError(rc)
+
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
+        t = time_launches(f, stream, reps)
+        fl = 2.0 * M * N * K * H
+        total_t += t
+        total_f += fl
+        per.append({"product": name, "M": M, "N": N, "K": K, "heads": H,
+                    "variant": ("t" if ta else "n") + ("t" if tb else "n"),
+                    "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2)})
+    return {"tokens": T, "head_dim": D, "heads": H, "dtype": "f16",
+            "total_us": round(total_t * 1e6, 2), "tflops": round(total_f / total_t / 1e12, 2),
+            "per_product": per}
+
+
+def epilogue_cost(dev, stream, reps):
+    """The MLP up-projection (512 x 5632 x 2048, nt, fp16) with and without the
+    fused bias + gelu epilogue: the epilogue's cost is the difference."""
+    import torch
+
+    import dense_gemm_amd as dg
+    import synth
+    M, N, K = 512, 5632, 2048
+    st = synth.Stream(41)
+    X = _dev_tensor(synth.round_to(st.normal((M, K)), "f16"), "f16", dev)
+    W = _dev_tensor(synth.round_to(st.normal((N, K), 0.02), "f16"), "f16", dev)
+    bias = _dev_tensor(synth.round_to(st.normal((N,), 0.5), "f16"), "f16", dev)
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    res = {"M": M, "N": N, "K": K, "variant": "nt", "dtype": "f16"}
+    for name, bp, epi in (("plain", None, dg.DG_EPI_NONE), ("bias_gelu", bias.data_ptr(), dg.DG_EPI_GELU),
+                          ("bias_relu", bias.data_ptr(), dg.DG_EPI_RELU)):
+        def f(bp=bp, epi=epi):
+            rc = dg.dg_gemm_ex(0, 1, M, N, K, 1.0, X.data_ptr(), K, 0, W.data_ptr(), K, 0, 0.0,
+                               Y.data_ptr(), N, 0, 1, bp, epi, dg.DG_F16_F32ACC, stream.cuda_stream)
+            if rc != 0:
+                raise dg.GemmError(rc)
+
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
+        t = min(time_launches(f, stream, reps) for _ in range(3))
+        res[name + "_us"] = round(t * 1e6, 2)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +362,18 @@ def main():
                          "traffic": measured_traffic(k16, ta, tb, S, S),
                          "algorithmic_bytes": 3 * S * S * 2}
         out["fp16_2048"] = {"peak": PEAK_F16, "unit": "TFLOP/s", **res}
+
+    # ---- bf16 2048^3 nn / tn / nt (same recipe as fp16) ------------------------
+    if not args.no_f16:
+        out["bf16_2048"] = bf16_square(dev, stream, max(args.steps, 200))
+
+    # ---- attention per-head products (strided batch over heads) ----------------
+    if not args.no_f16:
+        out["attention_heads"] = attention_heads(dev, stream, max(args.steps, 50))
+
+    # ---- fused epilogue on the MLP up-projection -----------------------------
+    if not args.no_f16:
+        out["epilogue"] = epilogue_cost(dev, stream, max(args.steps, 100))
 
     # ---- LoRA MLP-block step: the 18 fp16 GEMMs of one forward + backward -------
     if not args.no_lora:

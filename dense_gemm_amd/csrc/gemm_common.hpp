@@ -56,13 +56,34 @@ __device__ __forceinline__ void select_batch(GemmParams &p, int b)
     p.C = (T *)p.C + (int64_t)b * p.strideC;
 }
 
+// gelu(x) = x * Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2, in fp32.  erf by
+// the rational approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, eq. 7.1.26 (after Hastings): for z >= 0,
+//   erfc(z) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z), |error| <= 1.5e-7.
+// With q = erfc(|x| / sqrt 2): gelu = x (1 - q/2) for x >= 0 and x q / 2 for
+// x < 0, so the negative side never forms 1 - erf and keeps its relative
+// accuracy.  About a dozen instructions against a general erff's several
+// dozen, which matters because the epilogue runs once per output after the
+// K loop, with nothing to overlap it.
+__device__ __forceinline__ float gelu(float x)
+{
+    const float z = __builtin_fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.f));
+    float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+    poly = __builtin_fmaf(t, poly, 1.421413741f);
+    poly = __builtin_fmaf(t, poly, -0.284496736f);
+    poly = __builtin_fmaf(t, poly, 0.254829592f);
+    const float q = poly * t * __expf(-z * z);
+    return x >= 0.f ? x * __builtin_fmaf(-0.5f, q, 1.f) : 0.5f * x * q;
+}
+
 // The activation of the epilogue, in fp32.  relu keeps NaN (the comparison
-// is false for it); gelu is x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)) with the
-// device erff.
+// is false for it); gelu as above (NaN stays NaN).
 __device__ __forceinline__ float activate(int act, float x)
 {
     if (act == ACT_RELU) return x < 0.f ? 0.f : x;
-    if (act == ACT_GELU) return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
+    if (act == ACT_GELU) return gelu(x);
     return x;
 }
 
@@ -75,6 +96,39 @@ __device__ __forceinline__ float epilogue_value(const GemmParams &p, float acc, 
     if (p.beta != 0.f) v = __builtin_fmaf(p.beta, c_in, v);
     if (p.bias) v += (float)((const T *)p.bias)[col];
     return activate(p.act, v);
+}
+
+// The same for 16 consecutive columns col .. col+15 (all < N): the bias is
+// read with 16-byte loads when its address allows.
+template <typename T>
+__device__ __forceinline__ void epilogue_row16(const GemmParams &p, float (&v)[16], const float (&cin)[16],
+                                               int col)
+{
+    float b[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) b[e] = 0.f;
+    if (p.bias) {
+        const T *bp = (const T *)p.bias + col;
+        if (((uintptr_t)bp & 15) == 0) {
+            constexpr int PER = 16 / sizeof(T);
+            typedef T VT __attribute__((ext_vector_type(PER)));
+#pragma unroll
+            for (int c = 0; c < 16 / PER; ++c) {
+                const VT x = *(const VT *)(bp + c * PER);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) b[c * PER + e] = (float)x[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) b[e] = (float)bp[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float x = p.alpha * v[e];
+        if (p.beta != 0.f) x = __builtin_fmaf(p.beta, cin[e], x);
+        v[e] = activate(p.act, x + b[e]);
+    }
 }
 
 // Workgroup id -> (split, id of the tile within the split) and the split's

@@ -602,8 +602,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                     }
                 }
             }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] = epilogue_value<T>(p, v[e], cin[e], gcol + e);
+            epilogue_row16<T>(p, v, cin, gcol);
             if constexpr (HALF) {
                 V8 o0, o1;
 #pragma unroll

@@ -119,6 +119,27 @@ def test_epilogue_without_product(dg, dtype, act):
                        act=act))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+@pytest.mark.parametrize("kernel_kind", ["auto", "simple"])
+def test_activation_over_a_dense_range(dg, dtype, act, kernel_kind):
+    """alpha = beta = 0: every row is act(bias), with the bias swept densely
+    over [-12, 12] (the activation alone, both tails of gelu included), in
+    the no-product kernel; and a K = 1 product that lands on the same values
+    through the matrix-core (or generic) epilogue."""
+    N = 4096
+    xs = synth.round_to(np.linspace(-12.0, 12.0, N), dtype)
+    M = 8
+    a, b, _ = synth.problem(M, N, 1, dtype, "uniform", 240)
+    check_full(Problem(a, b, None, False, False, 0.0, 0.0, dtype, bias=xs, act=act))
+    # K = 1 product a * b with a = 1: act(b + 0) = act(x) for x = b
+    one = synth.round_to(np.ones((M, 1)), dtype)
+    bvals = xs.reshape(1, N)
+    k = -1 if kernel_kind == "auto" else dg.kernel_names().index(f"{dtype}_64x64_simple")
+    p = Problem(one, bvals, None, False, False, 1.0, 0.0, dtype, act=act)
+    check_full(p, kernel=k)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_epilogue_mlp_projection_sampled(dg, dtype):
     """The LoRA block's up-projection shape (512 x 5632 x 2048, nt) with a
