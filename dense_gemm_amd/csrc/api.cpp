@@ -61,13 +61,20 @@ const Family kFamilies[] = {
     {"bf16_128x128_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 0},
     {"bf16_256x128_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1},
     {"bf16_128x128_pipe2_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 2},
+    {"f16_64x64_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE, dg::f16_pipe_launchers, 3},
+    {"f16_128x32_pipe4_mfma32x32x16", DG_F16_F32ACC, 128, 32, 4, PIPE, dg::f16_pipe_launchers, 4},
+    {"f16_32x128_pipe4_mfma32x32x16", DG_F16_F32ACC, 32, 128, 4, PIPE, dg::f16_pipe_launchers, 5},
+    {"bf16_64x64_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE, dg::bf16_pipe_launchers, 3},
+    {"bf16_128x32_pipe4_mfma32x32x16", DG_BF16_F32ACC, 128, 32, 4, PIPE, dg::bf16_pipe_launchers, 4},
+    {"bf16_32x128_pipe4_mfma32x32x16", DG_BF16_F32ACC, 32, 128, 4, PIPE, dg::bf16_pipe_launchers, 5},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
     K_F32_SIMPLE = 0, K_F16_SIMPLE = 1, K_F32_256 = 2, K_F32_128 = 3, K_F16_128 = 4, K_F16_256 = 5,
     K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7, K_F16_PIPE_128_2 = 8, K_F32_PIPE_256x128 = 9,
     K_F32_PIPE_256x256 = 10, K_F32_PIPE_128 = 11, K_BF16_SIMPLE = 12, K_BF16_PIPE_128 = 13,
-    K_BF16_PIPE_256 = 14, K_BF16_PIPE_128_2 = 15
+    K_BF16_PIPE_256 = 14, K_BF16_PIPE_128_2 = 15, K_F16_PIPE_64 = 16, K_F16_PIPE_128x32 = 17,
+    K_F16_PIPE_32x128 = 18, K_BF16_PIPE_64 = 19, K_BF16_PIPE_128x32 = 20, K_BF16_PIPE_32x128 = 21
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -184,8 +191,20 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
     // pipeline; else the deep one-workgroup pipeline
     const bool bf = dtype == DG_BF16_F32ACC;
     if (pipe) {
+        // narrow outputs take tiles that match them instead of padding a
+        // 128-wide tile: N or M of 32 (low-rank products), 64 (attention's
+        // per-head products with d_head = 64)
+        if (N <= 32) return bf ? K_BF16_PIPE_128x32 : K_F16_PIPE_128x32;
+        if (M <= 32) return bf ? K_BF16_PIPE_32x128 : K_F16_PIPE_32x128;
+        if (N <= 64 || M <= 64) return bf ? K_BF16_PIPE_64 : K_F16_PIPE_64;
+        // a single K slab: writing C dominates, the large tile fills the GPU
+        // once there is one per CU (attention's Q K^T, measured)
+        if (K <= 64 && big >= 256) return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
         if (big >= 512) return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
         if (small >= 512) return bf ? K_BF16_PIPE_128_2 : K_F16_PIPE_128_2;
+        // fewer 128x128 tiles than half the CUs and K too short to split:
+        // smaller tiles (the LoRA K = 32 products, measured)
+        if (small < 128 && K < 1024) return bf ? K_BF16_PIPE_64 : K_F16_PIPE_64;
         return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
     }
     if (bf) return K_BF16_SIMPLE;

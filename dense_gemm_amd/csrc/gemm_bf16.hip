@@ -5,21 +5,29 @@
 
 namespace dg {
 
-// [config][transA * 2 + transB]
+// pipelined direct-to-LDS kernels: [config][transA * 2 + transB]
 //   0: 128x128 tile, 4 stages, two K groups of 4 waves (one workgroup per CU)
 //   1: 256x128 tile, 2 stages, eight 64x64 waves
 //   2: 128x128 tile, 2 stages, two K groups (two workgroups per CU)
+//   3: 64x64 tile, 4 stages, two K groups of two 64x32 waves (narrow outputs:
+//      attention's N = d_head products)
+//   4: 128x32 tile, 4 stages, four 32x32 waves (N = 32: low-rank products)
+//   5: 32x128 tile, 4 stages, four 32x32 waves (M = 32)
+#define DG_PIPE4(T, BM, BN, WM, WN, ST, KS)                                                   \
+    {launch_pipe<T, BM, BN, WM, WN, false, false, ST, KS>, launch_pipe<T, BM, BN, WM, WN, false, true, ST, KS>, \
+     launch_pipe<T, BM, BN, WM, WN, true, false, ST, KS>, launch_pipe<T, BM, BN, WM, WN, true, true, ST, KS>}
 const launch_fn *bf16_pipe_launchers(int config)
 {
-    static const launch_fn table[3][4] = {
-        {launch_pipe<__bf16, 128, 128, 64, 64, false, false, 4, 2>, launch_pipe<__bf16, 128, 128, 64, 64, false, true, 4, 2>,
-         launch_pipe<__bf16, 128, 128, 64, 64, true, false, 4, 2>, launch_pipe<__bf16, 128, 128, 64, 64, true, true, 4, 2>},
-        {launch_pipe<__bf16, 256, 128, 64, 64, false, false, 2, 1>, launch_pipe<__bf16, 256, 128, 64, 64, false, true, 2, 1>,
-         launch_pipe<__bf16, 256, 128, 64, 64, true, false, 2, 1>, launch_pipe<__bf16, 256, 128, 64, 64, true, true, 2, 1>},
-        {launch_pipe<__bf16, 128, 128, 64, 64, false, false, 2, 2>, launch_pipe<__bf16, 128, 128, 64, 64, false, true, 2, 2>,
-         launch_pipe<__bf16, 128, 128, 64, 64, true, false, 2, 2>, launch_pipe<__bf16, 128, 128, 64, 64, true, true, 2, 2>},
+    static const launch_fn table[6][4] = {
+        DG_PIPE4(__bf16, 128, 128, 64, 64, 4, 2),
+        DG_PIPE4(__bf16, 256, 128, 64, 64, 2, 1),
+        DG_PIPE4(__bf16, 128, 128, 64, 64, 2, 2),
+        DG_PIPE4(__bf16, 64, 64, 64, 32, 4, 2),
+        DG_PIPE4(__bf16, 128, 32, 32, 32, 4, 1),
+        DG_PIPE4(__bf16, 32, 128, 32, 32, 4, 1),
     };
     return table[config];
 }
+#undef DG_PIPE4
 
 }  // namespace dg

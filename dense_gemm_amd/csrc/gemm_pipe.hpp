@@ -25,7 +25,11 @@
 //     groups.  Fragments: one ds_read_b128 = 8 consecutive k of one row.
 //   m/n-contiguous operand (A transposed, B not transposed): [64][BMN]
 //     halfs, rows of BMN*2 bytes; the 64-byte quad q of row k sits at quad
-//     q ^ (k&3).  Fragments come from ds_read_b64_tr_b16, the hardware
+//     q ^ swz(k): k&3 when a row has 4 or more quads (BMN >= 128), (k>>1)&1
+//     when it has 2 (BMN = 64: rows 128 bytes = 32 banks apart, so rows k
+//     and k+2 would meet), none for BMN = 32 (64-byte rows already fall on
+//     distinct banks for the 4 rows a read takes).  Fragments come from
+//     ds_read_b64_tr_b16, the hardware
 //     transposing read: in each 16-lane group, lanes 4t..4t+3 name row t of a
 //     4 x 16 block and lane j receives column j, i.e. 4 consecutive k of its
 //     own m (or n) -- the MFMA operand layout -- with no write-side transpose
@@ -95,6 +99,14 @@ struct PipeOperandH {
     static_assert(LOADS * NW * 64 * 16 == BYTES, "slab must split into 16-byte loads");
     static constexpr int ROW_BYTES = KCONT ? PIPE_BK * 2 : BMN * 2;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide load fills
+    static constexpr int QUADS = ROW_BYTES / 64;             // 64-byte quads per row (m/n-contiguous)
+    static_assert(KCONT || BMN == 32 || BMN == 64 || BMN % 128 == 0, "m/n-contiguous tile width");
+
+    // XOR applied to the quad index of row k (m/n-contiguous layout)
+    __device__ static __forceinline__ int swz(int k)
+    {
+        return QUADS >= 4 ? (k & 3) : (QUADS == 2 ? ((k >> 1) & 1) : 0);
+    }
 
     const E *ptr[LOADS];         // per-lane global addresses of the current slab
     int64_t step;                // elements to advance per slab
@@ -116,7 +128,7 @@ struct PipeOperandH {
             } else {
                 const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
                 const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
-                const int q = (p >> 2) ^ (r & 3);                 // logical 64-byte quad
+                const int q = (p >> 2) ^ swz(r);                  // logical 64-byte quad
                 int col = mn0 + q * 32 + (p & 3) * 8;
                 col = col < ext ? col : ext - 8;
                 ptr[i] = g + (int64_t)r * ld + col;
@@ -191,8 +203,8 @@ struct PipeOperandH {
             const int q = b0 >> 5;
             const int colb = (16 * (g & 1) + 4 * s) * 2;   // byte offset inside the 64-byte quad
             const int k0 = 16 * kk + 8 * (g >> 1) + t;
-            const lds_char_t *p0 = lds + k0 * ROW_BYTES + ((q ^ t) << 6) + colb;
-            const lds_char_t *p1 = p0 + 4 * ROW_BYTES;      // rows k0 + 4 (same k & 3)
+            const lds_char_t *p0 = lds + k0 * ROW_BYTES + ((q ^ swz(k0)) << 6) + colb;
+            const lds_char_t *p1 = p0 + 4 * ROW_BYTES;      // rows k0 + 4 (same swizzle)
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
             typedef short i16x8 __attribute__((ext_vector_type(8)));
