@@ -52,7 +52,7 @@ def measured_traffic(kernel, ta, tb, M, N):
     table = {}
     for line in open(path):
         if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
+            k, v = line.rsplit("=", 1)
             table[k.strip()] = v.strip()
     if table.get("sources") != h.hexdigest()[:16]:
         return None
