@@ -183,12 +183,9 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
     const int64_t small = ceil_div(M, 128) * ceil_div(N, 128) * nb;
     const bool pipe = pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x);
     if (dtype == DG_F32) {
-        // 256x256 with eight waves once every CU gets a tile: measured at or
-        // above the 256x128 tile at 4096^3 and 8192^3 on every box tried
-        // (137-140 against 131-139 TFLOP/s at 4096^3), whose two workgroups
-        // per CU vary more from box to box
-        const int64_t huge = ceil_div(M, 256) * ceil_div(N, 256) * nb;
-        if (pipe && huge >= 256) return K_F32_PIPE_256x256;
+        // 256x128 with two workgroups per CU; the 256x256 eight-wave kernel
+        // measured the same on average over four boxes (each ahead on some:
+        // the spread follows the boxes' clocks, 2.16-2.40 GHz under load)
         if (pipe) return big >= 384 ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }

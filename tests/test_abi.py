@@ -121,7 +121,7 @@ def test_selection_picks_matrix_core_kernels_of_the_right_type():
             assert ("mfma" in name) == (dtype != 2 or aligned), (M, N, K, name)
     # the headline shapes get the large tiles
     k = dg.dg_select_kernel(0, 0, 4096, 4096, 4096, NULL, 4096, NULL, 4096, NULL, 4096, 0)
-    assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 256)
+    assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 128)
     k = dg.dg_select_kernel(0, 0, 2048, 2048, 2048, NULL, 2048, NULL, 2048, NULL, 2048, 1)
     assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (128, 128)
 
