@@ -52,14 +52,14 @@ const Family kFamilies[] = {
     {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, MFMA, dg::f16_launchers, 0},
     {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, MFMA, dg::f16_launchers, 1},
     {"f16_128x128_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0},
-    {"f16_256x128_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1},
+    {"f16_256x128_pipe3_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1},
     {"f16_128x128_pipe2_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 2},
     {"f32_256x128_pipe3_mfma32x32x2", DG_F32, 256, 128, 8, PIPE, dg::f32_pipe_launchers, 0},
     {"f32_256x256_pipe4_w8_mfma32x32x2", DG_F32, 256, 256, 4, PIPE, dg::f32_pipe_launchers, 1},
     {"f32_128x128_pipe4_mfma32x32x2", DG_F32, 128, 128, 8, PIPE, dg::f32_pipe_launchers, 2},
     {"bf16_64x64_simple", DG_BF16_F32ACC, 64, 64, 1, SIMPLE, nullptr, 0},
     {"bf16_128x128_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 0},
-    {"bf16_256x128_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1},
+    {"bf16_256x128_pipe3_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1},
     {"bf16_128x128_pipe2_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 2},
     {"f16_64x64_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE, dg::f16_pipe_launchers, 3},
     {"f16_128x32_pipe4_mfma32x32x16", DG_F16_F32ACC, 128, 32, 4, PIPE, dg::f16_pipe_launchers, 4},

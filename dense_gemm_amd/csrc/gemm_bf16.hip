@@ -7,7 +7,8 @@ namespace dg {
 
 // pipelined direct-to-LDS kernels: [config][transA * 2 + transB]
 //   0: 128x128 tile, 4 stages, two K groups of 4 waves (one workgroup per CU)
-//   1: 256x128 tile, 2 stages, eight 64x64 waves
+//   1: 256x128 tile, 3 stages, eight 64x64 waves (144 KB: one workgroup per
+//      CU, as with 2 stages, whose shorter prefetch measured 8% slower)
 //   2: 128x128 tile, 2 stages, two K groups (two workgroups per CU)
 //   3: 64x64 tile, 4 stages, two K groups of two 64x32 waves (narrow outputs:
 //      attention's N = d_head products)
@@ -20,7 +21,7 @@ const launch_fn *bf16_pipe_launchers(int config)
 {
     static const launch_fn table[6][4] = {
         DG_PIPE4(__bf16, 128, 128, 64, 64, 4, 2),
-        DG_PIPE4(__bf16, 256, 128, 64, 64, 2, 1),
+        DG_PIPE4(__bf16, 256, 128, 64, 64, 3, 1),
         DG_PIPE4(__bf16, 128, 128, 64, 64, 2, 2),
         DG_PIPE4(__bf16, 64, 64, 64, 32, 4, 2),
         DG_PIPE4(__bf16, 128, 32, 32, 32, 4, 1),

@@ -240,5 +240,5 @@ def test_ex_forced_kernel_checks():
 def test_bf16_kernels_listed():
     names = dg.kernel_names()
     for n in ("bf16_64x64_simple", "bf16_128x128_pipe4_ksplit2_mfma32x32x16",
-              "bf16_256x128_pipe2_w8_mfma32x32x16"):
+              "bf16_256x128_pipe3_w8_mfma32x32x16"):
         assert n in names
