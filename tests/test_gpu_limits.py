@@ -1,0 +1,92 @@
+"""Parity at the limits, on an MI355X through the C ABI: an output of more
+than 2^31 elements (64-bit offsets in every store path), thousands of
+batches in one call (the batch grid dimension), and a split-K over a very
+long K."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import Batched, sample_points
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dg():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_gemm_amd
+    return dense_gemm_amd
+
+
+@pytest.mark.parametrize("aligned", [True, False])
+def test_output_beyond_2_pow_31_elements(dg, aligned):
+    """C with 46400^2 (or 46341 x 46343, odd strides: element stores) fp16
+    elements, K small; sampled against the oracle, every element checked
+    finite on the device, the last row's tail included."""
+    import torch
+    dev = torch.device("cuda:0")
+    if aligned:
+        M, N, K, lda, ldc = 46400, 46400, 32, 32, 46400
+    else:
+        M, N, K, lda, ldc = 46341, 46343, 33, 35, 46345
+    assert M * N > 2 ** 31
+    a, b, _ = synth.problem(M, N, K, "f16", "uniform", 500)
+    A, _ = synth.store(a, False, lda)
+    B, ldb = synth.store(b, False)
+    At = torch.from_numpy(A).to(dev)
+    Bt = torch.from_numpy(B).to(dev)
+    Ct = torch.full((M, ldc), float("nan"), dtype=torch.float16, device=dev)
+    print(f"large output {M}x{N} aligned={aligned}", flush=True)
+    rc = dg.dg_gemm(0, 0, M, N, K, 1.0, At.data_ptr(), lda, Bt.data_ptr(), ldb, 0.0, Ct.data_ptr(),
+                    ldc, dg.DG_F16_F32ACC, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, dg.dg_status_string(rc)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Ct[:, :N]).all())
+    if ldc > N:
+        assert bool(torch.isnan(Ct[:, N:]).all())
+    rows, cols = sample_points(M, N, 3000, 501)
+    rows = np.concatenate([rows, [M - 1] * 4])
+    cols = np.concatenate([cols, [N - 1, N - 2, N - 17, 0]])
+    got = Ct[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)].float().cpu().numpy()
+    ref, ab = oracle.gemm_points(False, False, M, N, K, 1.0, A, lda, B, ldb, 0.0, None, ldc, rows,
+                                 cols)
+    worst, bad = oracle.compare("f16", got, ref, ab, 1.0, 0.0)
+    assert bad == 0, worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_thousands_of_batches(dg, dtype):
+    bp = Batched(24, 40, 16, dtype, 2000, False, True, 1.0, 0.5, 510, gap=(8, 8, 8),
+                 bias=synth.round_to(synth.Stream(511).uniform((40,)), dtype), act="relu")
+    bp.check(bp.run_gpu())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_splitk_very_long_k(dg, dtype):
+    """K = 40000 over an 96 x 80 output: the library's split choice, fp32
+    partials in a caller workspace, one reduction."""
+    import torch
+    dev = torch.device("cuda:0")
+    M, N, K = 96, 80, 40000
+    dist = "uniform" if dtype == "f32" else "normal_sqrtk"
+    a, b, c0 = synth.problem(M, N, K, dtype, dist, 520, with_c0=True)
+    tdt = torch.float32 if dtype == "f32" else torch.float16
+    A = torch.from_numpy(a).to(dev)
+    B = torch.from_numpy(b).to(dev)
+    C = torch.from_numpy(c0.copy()).to(dev)
+    code = dg.DG_F32 if dtype == "f32" else dg.DG_F16_F32ACC
+    splits = dg.dg_gemm_splitk_choose(0, 0, M, N, K, code)
+    assert splits > 1
+    wsb = dg.dg_gemm_splitk_workspace_size(M, N, splits)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    rc = dg.dg_gemm_splitk(0, 0, M, N, K, 0.5, A.data_ptr(), K, B.data_ptr(), N, -1.0, C.data_ptr(),
+                           N, code, torch.cuda.current_stream().cuda_stream, 0, ws.data_ptr(), wsb)
+    assert rc == 0, dg.dg_status_string(rc)
+    torch.cuda.synchronize()
+    assert C.dtype == tdt
+    ref, ab = oracle.gemm(False, False, M, N, K, 0.5, a, K, b, N, -1.0, c0, N)
+    worst, bad = oracle.compare(dtype, C.float().cpu().numpy(), ref, ab, 0.5, -1.0, c0)
+    assert bad == 0, worst
