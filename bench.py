@@ -107,9 +107,10 @@ def lora_step(dev, stream, reps):
 
         splits = dg.dg_gemm_splitk_choose(ta, tb, M, N, K, dg.DG_F16_F32ACC)
 
-        def f(ta=ta, tb=tb, M=M, N=N, K=K, A=A, B=B, C=C, lda=lda, ldb=ldb, beta=beta):
+        def f(ta=ta, tb=tb, M=M, N=N, K=K, A=A, B=B, C=C, lda=lda, ldb=ldb, beta=beta, stream_ptr=None):
             rc = dg.dg_gemm_splitk(ta, tb, M, N, K, 1.0, A.data_ptr(), lda, B.data_ptr(), ldb, beta,
-                                   C.data_ptr(), N, dg.DG_F16_F32ACC, sptr, 0, ws.data_ptr(),
+                                   C.data_ptr(), N, dg.DG_F16_F32ACC,
+                                   sptr if stream_ptr is None else stream_ptr, 0, ws.data_ptr(),
                                    ws.numel() * 4)
             if rc != 0:
                 raise dg.GemmError(rc)
@@ -124,6 +125,19 @@ def lora_step(dev, stream, reps):
     torch.cuda.synchronize()
     t_step = time_launches(step, stream, reps)
     flops = sum(2.0 * M * N * K for _, M, N, K, _, _ in calls)
+
+    # the same step captured once in a HIP graph and replayed: the library
+    # only enqueues kernels on the caller's stream (no allocation, no memset),
+    # so a whole step records; replay takes the host's per-launch cost off the
+    # GPU's critical path
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for name, M, N, K, f, _ in calls:
+            f(stream_ptr=torch.cuda.current_stream(dev).cuda_stream)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_graph = time_launches(graph.replay, stream, reps)
     per = []
     for name, M, N, K, f, kname in calls:
         t = time_launches(f, stream, reps)
@@ -131,7 +145,9 @@ def lora_step(dev, stream, reps):
                     "tflops": round(2.0 * M * N * K / t / 1e12, 2), "kernel": kname})
     return {"step_ms": round(t_step * 1e3, 4), "gflop": round(flops / 1e9, 3),
             "tflops": round(flops / t_step / 1e12, 2),
-            "tokens_per_s": round(512 / t_step, 1), "per_gemm": per}
+            "tokens_per_s": round(512 / t_step, 1),
+            "graph_step_ms": round(t_graph * 1e3, 4), "graph_tflops": round(flops / t_graph / 1e12, 2),
+            "per_gemm": per}
 
 
 def _dev_tensor(x, dtype, dev):
