@@ -11,7 +11,12 @@ tn and nt variants (entries N(0,1)/sqrt(K) rounded to fp16, seed 2).
 
 `roofline` is for the fp32 kernel: achieved TFLOP/s = 2*M*N*K per launch /
 mean launch duration, timed with events recorded on the stream the kernel runs
-on, against the MI355X dense fp32 matrix peak (157.3 TFLOP/s).  `cpu_baseline`
+on, against the MI355X dense fp32 matrix peak (157.3 TFLOP/s), and against the
+matrix-core rate the control probe measures on the same box.  `control` holds
+the control benchmarks (matrix-core peak with the shader clock under load, and
+a plain copy) and whether they are within 10% of their references;
+`per_launch_us` and `cold_us` give per-launch medians, best and worst, and the
+median after a 512 MiB cache scrub.  `cpu_baseline`
 times the CPU oracle (plain fp64 triple loop, all host cores) on a bounded
 sample of the same workload: whole rows of C.
 """
@@ -30,6 +35,16 @@ PEAK_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix
 PEAK_F16 = 2516.6     # TFLOP/s, MI355X dense fp16 matrix
 HBM_PEAK = 8000.0     # GB/s
 
+# Control benchmarks and their references.  "Metal GEMM Kernels for LoRA
+# Training on Apple Silicon", section 9: a performance figure is trusted only
+# while a control benchmark stays within 10% of its reference.  The matrix-core
+# probes' references are the published peaks; the copy's is the read + write
+# rate a plain copy sustains on this part (4.6 TB/s of the 8 TB/s peak).
+REF_MFMA_F32 = PEAK_F32
+REF_MFMA_F16 = PEAK_F16
+REF_COPY_GBS = 4600.0
+CONTROL_TOL = 0.10
+
 
 def tflops(M, N, K, seconds):
     return 2.0 * M * N * K / seconds / 1e12
@@ -47,11 +62,12 @@ def measured_traffic(kernel, ta, tb, M, N):
     if not os.path.exists(path):
         return None
     h = hashlib.sha256()
-    # the kernels' sources only: the dispatcher (api.cpp) picks kernels but does
-    # not change what a given kernel moves
+    # the GEMM kernels' sources only: the dispatcher (api.cpp) picks kernels but
+    # does not change what a given kernel moves, and probe.hip holds no GEMM
     for f in sorted(glob.glob(os.path.join(ROOT, "dense_gemm_amd", "csrc", "*.hip")) +
                     glob.glob(os.path.join(ROOT, "dense_gemm_amd", "csrc", "*.hpp"))):
-        h.update(open(f, "rb").read())
+        if os.path.basename(f) != "probe.hip":
+            h.update(open(f, "rb").read())
     table = {}
     for line in open(path):
         if "=" in line and not line.startswith("#"):
@@ -76,6 +92,93 @@ def time_launches(fn, stream, reps):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / 1e3 / reps
+
+
+def per_launch(fn, stream, n):
+    """Per-launch durations (µs) from an event pair around each of n launches
+    on `stream`: median, best and worst."""
+    import statistics
+    import torch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for a, b in pairs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    pairs[-1][1].synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    return {"median": round(statistics.median(us), 2), "best": round(min(us), 2),
+            "worst": round(max(us), 2), "launches": n}
+
+
+def cold_launches(fn, stream, n, scrub):
+    """Median duration (µs) of n launches, each after `scrub` (a 512 MiB
+    buffer, twice the Infinity Cache) is rewritten on the same stream, so the
+    operands come from HBM instead of the caches."""
+    import statistics
+    import torch
+    us = []
+    for i in range(n):
+        scrub.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        us.append(a.elapsed_time(b) * 1e3)
+    return round(statistics.median(us), 2)
+
+
+def control_probes(dev, stream):
+    """The control benchmarks (libdense_gemm_probe.so): matrix-core peak of the
+    fp32 and fp16 instructions the GEMMs use, with the shader clock while they
+    run, and the plain-copy HBM rate; each against its reference."""
+    import statistics
+    import torch
+
+    import dense_gemm_amd.probe as pr
+
+    sptr = stream.cuda_stream
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count   # two waves per SIMD
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
+    khz = pr.dgp_wall_clock_khz()
+    res = {}
+    for name, kind, iters in (("mfma_f32", pr.DGP_MFMA_F32, 8000), ("mfma_f16", pr.DGP_MFMA_F16, 16000)):
+        def f(kind=kind, iters=iters):
+            rc = pr.dgp_mfma_peak(kind, wgs, iters, sink.data_ptr(), clocks.data_ptr(), sptr)
+            if rc != 0:
+                raise RuntimeError(f"dgp_mfma_peak failed ({rc}, hip {pr.dgp_last_hip_error()})")
+        f()
+        torch.cuda.synchronize()
+        t = min(time_launches(f, stream, 3) for _ in range(3))
+        c = clocks.view(wgs, 2).cpu().numpy()
+        ratio = statistics.median(float(x) / float(y) for x, y in c if y > 0)
+        res[name] = {"tflops": round(pr.dgp_mfma_flops(kind, wgs, iters) / t / 1e12, 1),
+                     "clock_mhz": round(ratio * khz / 1e3) if khz > 0 else None}
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def cp():
+        rc = pr.dgp_copy(src.data_ptr(), dst.data_ptr(), nbytes, sptr)
+        if rc != 0:
+            raise RuntimeError(f"dgp_copy failed ({rc}, hip {pr.dgp_last_hip_error()})")
+    cp()
+    torch.cuda.synchronize()
+    t = min(time_launches(cp, stream, 5) for _ in range(2))
+    assert bool(torch.equal(src[:: 1 << 20], dst[:: 1 << 20]))
+    del src, dst
+    gbs = 2 * nbytes / t / 1e9
+    ok = (res["mfma_f32"]["tflops"] >= (1 - CONTROL_TOL) * REF_MFMA_F32
+          and res["mfma_f16"]["tflops"] >= (1 - CONTROL_TOL) * REF_MFMA_F16
+          and gbs >= (1 - CONTROL_TOL) * REF_COPY_GBS)
+    return {"mfma_f32_tflops": res["mfma_f32"]["tflops"], "mfma_f32_clock_mhz": res["mfma_f32"]["clock_mhz"],
+            "mfma_f16_tflops": res["mfma_f16"]["tflops"], "mfma_f16_clock_mhz": res["mfma_f16"]["clock_mhz"],
+            "copy_gbs": round(gbs, 1),
+            "references": {"mfma_f32_tflops": REF_MFMA_F32, "mfma_f16_tflops": REF_MFMA_F16,
+                           "copy_gbs": REF_COPY_GBS, "tolerance": CONTROL_TOL},
+            "within_tolerance": bool(ok)}
 
 
 def lora_step(dev, stream, reps):
@@ -277,6 +380,9 @@ def main():
     ap.add_argument("--no-lora", action="store_true", help="skip the LoRA-step GEMM sequence")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache launches (for hardware-counter passes, whose "
+                         "per-kernel averages would otherwise mix cold and warm launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device-to-device copy (a kernel of known traffic, "
                          "to scale hardware byte counters)")
@@ -296,6 +402,8 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
+
+    control = control_probes(dev, stream)
 
     if args.copy_calibration:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
@@ -330,6 +438,9 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = tflops(M, N, K, wall / args.steps)
     achieved = tflops(M, N, K, launch_s)
+    f32_launches = per_launch(step, stream, 20)
+    scrub = None if args.no_cold else torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+    f32_cold_us = None if args.no_cold else cold_launches(step, stream, 5, scrub)   # 512 MiB scrub
 
     out = {
         "metric": "TFLOP/s + % of MFMA peak: fp32 4096^3 nn; fp16->fp32 2048^3 nn/tn/nt",
@@ -349,8 +460,16 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32, 4),
                      "traffic": measured_traffic(kernel, 0, 0, M, N),
-                     "algorithmic_bytes": 3 * M * N * 4, "kernel_ms": round(launch_s * 1e3, 4)},
+                     "algorithmic_bytes": 3 * M * N * 4, "kernel_ms": round(launch_s * 1e3, 4),
+                     "frac_of_probe_peak": round(achieved / control["mfma_f32_tflops"], 4),
+                     "probe_clock_mhz": control["mfma_f32_clock_mhz"]},
+        "per_launch_us": f32_launches,
+        "cold_us": f32_cold_us,
+        "control": control,
     }
+    if not control["within_tolerance"]:
+        out["gate"] = ("a control benchmark is more than 10% from its reference: "
+                       "the figures of this line are not trusted")
 
     # ---- fp16 2048^3 nn / tn / nt ---------------------------------------------
     if not args.no_f16:
@@ -377,9 +496,12 @@ def main():
             t16 = min(time_launches(step16, stream, reps) for _ in range(3))
             ach = tflops(S, S, S, t16)
             res[name] = {"tflops": round(ach, 2), "frac": round(ach / PEAK_F16, 4),
+                         "frac_of_probe_peak": round(ach / control["mfma_f16_tflops"], 4),
                          "kernel_us": round(t16 * 1e6, 2), "kernel": dg.dg_kernel_name(k16),
                          "traffic": measured_traffic(k16, ta, tb, S, S),
-                         "algorithmic_bytes": 3 * S * S * 2}
+                         "algorithmic_bytes": 3 * S * S * 2,
+                         "per_launch_us": per_launch(step16, stream, 100),
+                         "cold_us": None if args.no_cold else cold_launches(step16, stream, 20, scrub)}
         out["fp16_2048"] = {"peak": PEAK_F16, "unit": "TFLOP/s", **res}
 
     # ---- bf16 2048^3 nn / tn / nt (same recipe as fp16) ------------------------

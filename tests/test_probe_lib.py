@@ -1,0 +1,114 @@
+"""The control-probe library (libdense_gemm_probe.so, include/dense_gemm_probe.h):
+on the CPU it loads, exports every declared symbol, counts its flops in closed
+form and rejects invalid arguments before any HIP call; on a GPU its copy is
+exact and its matrix-core probe reports a plausible rate and shader clock."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_gemm_amd.probe as pr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dense_gemm_probe.h")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(dgp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(pr.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", pr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    lib = ctypes.CDLL(pr.LIB_PATH)
+    for name in declared_functions():
+        assert name in syms, name
+        assert hasattr(lib, name), name
+
+
+def test_header_compiles_as_c99(tmp_path):
+    src = tmp_path / "p.c"
+    refs = "\n".join(f"    (void)&{f};" for f in declared_functions())
+    src.write_text(f'#include "dense_gemm_probe.h"\nint main(void) {{\n{refs}\n    return DGP_MFMA_F32;\n}}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                    "-I", os.path.dirname(HEADER), str(src)], check=True, capture_output=True, text=True)
+
+
+def test_flop_count_closed_form():
+    # 8 MFMAs per round, 4 waves per workgroup; 2*32*32*2 and 2*32*32*16 flops each
+    assert pr.dgp_mfma_flops(pr.DGP_MFMA_F32, 512, 1000) == 512 * 4 * 1000 * 8 * 4096
+    assert pr.dgp_mfma_flops(pr.DGP_MFMA_F16, 3, 7) == 3 * 4 * 7 * 8 * 32768
+    assert pr.dgp_mfma_flops(9, 512, 1000) == 0.0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 512, 10), -1),
+    ((pr.DGP_MFMA_F32, 0, 10), -2),
+    ((pr.DGP_MFMA_F32, 65537, 10), -2),
+    ((pr.DGP_MFMA_F16, 4, 0), -3),
+    ((pr.DGP_MFMA_F16, 4, (1 << 24) + 1), -3),
+])
+def test_mfma_probe_invalid_arguments(args, code):
+    assert pr.dgp_mfma_peak(*args, 16, 16, None) == code
+
+
+def test_mfma_probe_null_buffers():
+    assert pr.dgp_mfma_peak(pr.DGP_MFMA_F32, 4, 10, None, 16, None) == -4
+    assert pr.dgp_mfma_peak(pr.DGP_MFMA_F32, 4, 10, 16, None, None) == -5
+
+
+def test_copy_invalid_arguments():
+    assert pr.dgp_copy(None, 16, 16, None) == -1
+    assert pr.dgp_copy(8, 16, 16, None) == -1            # not 16-byte aligned
+    assert pr.dgp_copy(16, None, 16, None) == -2
+    assert pr.dgp_copy(16, 24, 16, None) == -2
+    assert pr.dgp_copy(16, 32, 15, None) == -3
+    assert pr.dgp_copy(16, 32, -16, None) == -3
+    assert pr.dgp_copy(16, 32, 0, None) == 0              # empty: nothing enqueued
+
+
+@pytest.mark.gpu
+def test_copy_is_exact():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    n = (3 << 20) + 4                                       # not a multiple of the block size
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.full((n + 4,), -1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    assert pr.dgp_copy(src.data_ptr(), dst.data_ptr(), n * 4, s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src)
+    assert bool((dst[n:] == -1).all())                    # nothing past the end
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind", [pr.DGP_MFMA_F32, pr.DGP_MFMA_F16])
+def test_mfma_probe_runs(kind):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    wgs, iters = 64, 200
+    sink = torch.full((wgs * 256,), float("nan"), dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
+    s = torch.cuda.current_stream()
+    print(f"mfma probe kind={kind} wgs={wgs} iters={iters}", flush=True)
+    assert pr.dgp_mfma_peak(kind, wgs, iters, sink.data_ptr(), clocks.data_ptr(), s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(sink).all())
+    c = clocks.view(wgs, 2).cpu()
+    assert bool((c > 0).all())
+    khz = pr.dgp_wall_clock_khz()
+    assert khz > 0
+    mhz = (c[:, 0].double() / c[:, 1].double()).median().item() * khz / 1e3
+    assert 500 < mhz < 3000, mhz                           # a shader clock, in MHz
