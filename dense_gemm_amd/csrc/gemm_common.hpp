@@ -131,6 +131,100 @@ __device__ __forceinline__ void epilogue_row16(const GemmParams &p, float (&v)[1
     }
 }
 
+// Split-K reduction of 16 consecutive columns c0 .. c0+15 of row `row` (only
+// those below N): the splits' fp32 partials (ws[s] is M x N, row stride N)
+// summed in increasing s starting from zero, then alpha, beta, bias and the
+// activation in fp32 and one rounding to T.  beta == 0 does not read C.
+// Partials are read with 16-byte loads when N is a multiple of 4 (the
+// workspace is 16-byte aligned), four splits' loads in flight at once; C is
+// written with 16-byte stores when its rows allow.
+template <typename T>
+__device__ __forceinline__ void reduce_group16(const GemmParams &p, int64_t row, int c0)
+{
+    typedef T V8 __attribute__((ext_vector_type(8)));
+    const int64_t mn = (int64_t)p.M * p.N;
+    const float *wrow = p.ws + row * p.N;
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    const bool full = c0 + 16 <= p.N;
+    if (full && (p.N & 3) == 0) {
+        int sp = 0;
+        for (; sp + 4 <= p.splits; sp += 4) {
+            f32x4 x[4][4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[u][q] = *(const f32x4 *)(wrow + (sp + u) * mn + c0 + 4 * q);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[4 * q + e] += x[u][q][e];
+        }
+        for (; sp < p.splits; ++sp) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 x = *(const f32x4 *)(wrow + sp * mn + c0 + 4 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * q + e] += x[e];
+            }
+        }
+    } else {
+        for (int sp = 0; sp < p.splits; ++sp)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (c0 + e < p.N) acc[e] += wrow[sp * mn + c0 + e];
+    }
+    T *c = (T *)p.C + row * p.ldc + c0;
+    if (full && p.c_vec) {
+        float cin[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cin[e] = 0.f;
+        if constexpr (sizeof(T) == 2) {
+            if (p.beta != 0.f) {
+                const V8 c0v = *(const V8 *)c, c1v = *(const V8 *)(c + 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    cin[e] = (float)c0v[e];
+                    cin[8 + e] = (float)c1v[e];
+                }
+            }
+            epilogue_row16<T>(p, acc, cin, c0);
+            V8 o0, o1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o0[e] = (T)acc[e];
+                o1[e] = (T)acc[8 + e];
+            }
+            *(V8 *)c = o0;
+            *(V8 *)(c + 8) = o1;
+        } else {
+            if (p.beta != 0.f) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 x = *(const f32x4 *)(c + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cin[4 * q + e] = x[e];
+                }
+            }
+            epilogue_row16<T>(p, acc, cin, c0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *(f32x4 *)(c + 4 * q) = (f32x4){acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (c0 + e < p.N) {
+                const float cin = p.beta != 0.f ? (float)c[e] : 0.f;
+                c[e] = (T)epilogue_value<T>(p, acc[e], cin, c0 + e);
+            }
+        }
+    }
+}
+
 // Workgroup id -> (split, id of the tile within the split) and the split's
 // k range [k_begin, k_begin + k_len).
 __device__ __forceinline__ void split_of(const GemmParams &p, int &bid, int &split, int &k_begin,

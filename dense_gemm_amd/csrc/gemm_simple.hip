@@ -121,52 +121,31 @@ __global__ __launch_bounds__(256) void scale_c_kernel(GemmParams p)
     }
 }
 
-// Split-K reduction: C = alpha * sum_s ws[s] + beta * C (ws[s] is M x N,
-// row stride N; splits summed in increasing s), one rounding to T.  beta == 0
-// does not read C.  Four consecutive columns per thread.
+// Split-K reduction (the second kernel of dg_gemm_splitk): C =
+// act(alpha * sum_s ws[s] + beta * C + bias), the splits summed in increasing
+// s (reduce_group16).  A thread takes 16 consecutive columns of one row; a
+// row has 2^tpr_log2 threads (enough to cover N / 16 groups, at most 256), a
+// workgroup 256 >> tpr_log2 rows, so the row and column come from shifts.
 template <typename T>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p)
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int tpr_log2)
 {
-    T *C = (T *)p.C;
-    const int64_t mn = (int64_t)p.M * p.N;
-    const int64_t groups = (mn + 3) / 4;
-    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups;
-         g += (int64_t)gridDim.x * 256) {
-        const int64_t e0 = g * 4;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        if ((p.N & 3) == 0) {
-            for (int sp = 0; sp < p.splits; ++sp) {
-                const f32x4 x = *(const f32x4 *)(p.ws + sp * mn + e0);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[u] += x[u];
-            }
-        } else {
-            for (int sp = 0; sp < p.splits; ++sp)
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (e0 + u < mn) acc[u] += p.ws[sp * mn + e0 + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t e = e0 + u;
-            if (e < mn) {
-                const int64_t i = e / p.N, j = e - i * p.N;
-                T *c = C + i * p.ldc + j;
-                const float cin = p.beta != 0.f ? to_f32(*c) : 0.f;
-                *c = (T)epilogue_value<T>(p, acc[u], cin, (int)j);
-            }
-        }
-    }
+    const int tpr = 1 << tpr_log2;
+    const int64_t row = (int64_t)blockIdx.x * (256 >> tpr_log2) + (threadIdx.x >> tpr_log2);
+    if (row >= p.M) return;
+    for (int c0 = (threadIdx.x & (tpr - 1)) * 16; c0 < p.N; c0 += tpr * 16) reduce_group16<T>(p, row, c0);
 }
 
 template <typename T>
 hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t s)
 {
-    const int64_t groups = ((int64_t)p.M * p.N + 3) / 4;
-    int64_t blocks = (groups + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    const int64_t groups = ((int64_t)p.N + 15) / 16;          // 16-column groups per row
+    int tpr_log2 = 0;
+    while (tpr_log2 < 8 && ((int64_t)1 << tpr_log2) < groups) ++tpr_log2;
+    const int64_t rows_per_block = 256 >> tpr_log2;
+    const int64_t blocks = ((int64_t)p.M + rows_per_block - 1) / rows_per_block;
     GemmParams arg = p;
-    void *args[] = {&arg};
+    int tl = tpr_log2;
+    void *args[] = {&arg, &tl};
     return hipLaunchKernel((const void *)&splitk_reduce_kernel<T>, dim3((unsigned)blocks), dim3(256),
                            args, 0, s);
 }

@@ -305,7 +305,10 @@ DT = {"f32": 0, "f16": 1}
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("ta,tb", TRANS)
 @pytest.mark.parametrize("shape,splits", [((200, 40, 1000), 0), ((72, 264, 777), 3), ((136, 32, 640), 7),
-                                          ((96, 96, 64), 2), ((520, 48, 2048), 0)])
+                                          ((96, 96, 64), 2), ((520, 48, 2048), 0),
+                                          # N not a multiple of 4 (element loads of the partials);
+                                          # N > 4096 (a reduction thread takes several column groups)
+                                          ((100, 37, 900), 3), ((40, 5000, 1024), 2)])
 def test_splitk(dg, dtype, ta, tb, shape, splits):
     M, N, K = shape
     a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 180 + 2 * ta + tb, with_c0=True)
