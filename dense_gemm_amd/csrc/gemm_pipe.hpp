@@ -180,14 +180,19 @@ struct PipeOperandH {
     __device__ __forceinline__ void issue(lds_char_t *lds, int wave)
     {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
-            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                         :
-                         : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
-                         : "memory");
-            ptr[i] += step;
-        }
+        for (int i = 0; i < LOADS; ++i) issue_one(lds, wave, i);
+    }
+
+    // Load i of this slab alone (the main loop spreads a slab's loads
+    // between its MFMAs).
+    __device__ __forceinline__ void issue_one(lds_char_t *lds, int wave, int i)
+    {
+        const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                     : "memory");
+        ptr[i] += step;
     }
 
     // MFMA operand of block rows [b0, b0+32) for k-step kk (16 k) of a stage.
@@ -443,15 +448,38 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             if (kt + STAGES <= nk) wait_vmcnt<(STAGES - 2) * LOADS>();
             else wait_vmcnt<0>();
             __syncthreads();
-            if (kt + STAGES < nk) issue_slab(kt + STAGES, smem + (kt % STAGES) * STAGE_BYTES);
+            // slab kt+STAGES goes into the stage of slab kt (whose fragments
+            // are in registers).  With both operands k-contiguous (nt) a
+            // regular slab's loads are spread between this slab's MFMAs, load
+            // l before MFMA l*NM/LOADS: direct loads issued in a burst stall
+            // the matrix core of their SIMD more than the same loads
+            // interleaved with its MFMAs.  With a transposed-read operand
+            // (nn, tn) the spread loads slowed the kernel instead (measured
+            // 3-21%), so there they go in one burst.  A partial last slab
+            // goes through registers, all at once.
+            constexpr bool SPREAD = !TA && TB;
+            const int ns = kt + STAGES;
+            lds_char_t *dst = smem + (kt % STAGES) * STAGE_BYTES;
+            const bool spread = SPREAD && ns < nk && !(ns == nk - 1 && krem < BK);
+            if (ns < nk && !spread) issue_slab(ns, dst);
             read(kt + 1, na, nb);
+            constexpr int NM = KPW * TM * TN;
 #pragma unroll
             for (int s = 0; s < KPW; ++s)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
+                    for (int j = 0; j < TN; ++j) {
+                        const int m = (s * TM + i) * TN + j;
+#pragma unroll
+                        for (int l = 0; l < (SPREAD ? LOADS : 0); ++l) {
+                            if (l * NM / LOADS == m && spread) {
+                                if (l < OpA::LOADS) ga.issue_one(dst, wave, l);
+                                else gb.issue_one(dst + OpA::BYTES, wave, l - OpA::LOADS);
+                            }
+                        }
                         acc[i][j] = mfma_32x32x16(ca[s][i], cb[s][j], acc[i][j]);
+                    }
         };
         if (nk > 0) {
             if (nk >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
