@@ -208,6 +208,15 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // fewer 128x128 tiles than half the CUs and K too short to split:
         // smaller tiles (the LoRA K = 32 products, measured)
         if (small < 128 && K < 1024) return bf ? K_BF16_PIPE_64 : K_F16_PIPE_64;
+        // at most half the CUs with a 128x128 tile while 64x64 tiles cover
+        // them all: the 64x64 kernel without a K split.  Measured at 512x2048,
+        // 1024x1024, 768x1536 and 512x4096 for K from 1024 to 8192: 7.7 us
+        // against 24.5 for the 128x128 tile split four ways at K = 1024 (the
+        // fp32 partials outweigh the output), 26 against 31 at K = 5632 (the
+        // LoRA down and dH products).  From K = 16384 the split 128x128 tile
+        // wins again (56 against 66 us).
+        const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64) * nb;
+        if (small <= 128 && t64 >= 256 && K <= 8192) return bf ? K_BF16_PIPE_64 : K_F16_PIPE_64;
         return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
     }
     if (bf) return K_BF16_SIMPLE;

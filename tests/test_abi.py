@@ -126,6 +126,26 @@ def test_selection_picks_matrix_core_kernels_of_the_right_type():
     assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (128, 128)
 
 
+def tile_of(M, N, K, dtype=1):
+    k = dg.dg_select_kernel(0, 0, M, N, K, 256, K, 256, N, 256, N, dtype)
+    return dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)
+
+
+def test_underfilled_16bit_grids_take_64x64_tiles_unsplit():
+    # at most 128 tiles of 128x128 but >= 256 of 64x64, K <= 8192: 64x64, no split
+    for dtype in (1, 2):
+        for M, N, K in ((512, 2048, 5632), (512, 2048, 1024), (1024, 1024, 4096), (512, 4096, 4096)):
+            assert tile_of(M, N, K, dtype) == (64, 64), (M, N, K, dtype)
+            assert dg.dg_gemm_splitk_choose(0, 0, M, N, K, dtype) == 1
+    # longer K: the 128x128 tile split over K
+    assert tile_of(512, 2048, 16384) == (128, 128)
+    assert dg.dg_gemm_splitk_choose(0, 0, 512, 2048, 16384, 1) > 1
+    # enough 128x128 tiles (176 for the LoRA gate projection): unchanged
+    assert tile_of(512, 5632, 2048) == (128, 128)
+    # fp32 is not affected
+    assert tile_of(512, 2048, 5632, 0) != (64, 64)
+
+
 def test_tile_grid_matches_the_pages_decompositions():
     """Output tiles of side T cover C[35,93] at ((35//T)*T, (93//T)*T): the
     8x8 tile at (32,88) entry (3,5) and the 64x64 tile at (0,64) of the pages
