@@ -408,9 +408,17 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             gb.issue(st + OpA::BYTES, wave);
         }
     };
-    // fp16 keeps STAGES slabs in flight, fp32 STAGES - 1 (see the loops below)
+    // 16-bit tiles of at least 128 x 128 with 4 or more stages: each step
+    // refills the stage consumed two steps earlier (LAG2, see the loop; on
+    // the 128 x 128 kernel 1-7.5% faster, most for tn, whose transposed reads
+    // of both operands made the barrier's wait for them longest; on the
+    // narrow tiles 2-10% slower).  Otherwise each step refills the stage
+    // consumed one step earlier.  The prologue issues the slabs the first
+    // step does not issue itself.
+    constexpr bool LAG2 = HALF && STAGES >= 4 && BM >= 128 && BN >= 128;
+    constexpr int PRO = (HALF && !LAG2) ? STAGES : STAGES - 1;
 #pragma unroll
-    for (int s = 0; s < (HALF ? STAGES : STAGES - 1); ++s) {
+    for (int s = 0; s < PRO; ++s) {
         if (s < nk) issue_slab(s, smem + s * STAGE_BYTES);
     }
 
@@ -444,12 +452,29 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
         };
         auto step = [&](int kt, V8(&ca)[KPW][TM], V8(&cb)[KPW][TN], V8(&na)[KPW][TM],
                         V8(&nb)[KPW][TN]) {
-            // slabs issued so far: [0, min(nk, kt + STAGES)); slab kt+1 must be complete
-            if (kt + STAGES <= nk) wait_vmcnt<(STAGES - 2) * LOADS>();
+            // slabs issued so far: [0, min(nk, kt + PRO)); slab kt+1 must be
+            // complete, in every wave's part
+            constexpr int AHEAD = PRO - 2;           // slabs that may stay in flight
+            if (kt + PRO <= nk) wait_vmcnt<AHEAD * LOADS>();
             else wait_vmcnt<0>();
-            __syncthreads();
-            // slab kt+STAGES goes into the stage of slab kt (whose fragments
-            // are in registers).  With both operands k-contiguous (nt) a
+            if constexpr (LAG2) {
+                // A bare barrier: it does not wait for this wave's fragment
+                // reads of slab kt+1 (issued in the previous step, first used
+                // by the next step's MFMAs), so they complete while the waves
+                // meet.  Safe because the loads issued below go into the stage
+                // of slab kt-1, whose fragments every wave has consumed in its
+                // MFMAs of the previous step.  The empty asm statements keep
+                // the compiler from moving LDS reads across the barrier.
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            } else {
+                // the loads below go into the stage of slab kt, whose fragment
+                // reads must be complete in every wave
+                __syncthreads();
+            }
+            // slab kt+PRO goes into the stage of slab kt-1 (LAG2) or kt.  With
+            // both operands k-contiguous (nt) a
             // regular slab's loads are spread between this slab's MFMAs, load
             // l before MFMA l*NM/LOADS: direct loads issued in a burst stall
             // the matrix core of their SIMD more than the same loads
@@ -458,8 +483,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             // 3-21%), so there they go in one burst.  A partial last slab
             // goes through registers, all at once.
             constexpr bool SPREAD = !TA && TB;
-            const int ns = kt + STAGES;
-            lds_char_t *dst = smem + (kt % STAGES) * STAGE_BYTES;
+            const int ns = kt + PRO;
+            lds_char_t *dst = smem + (ns % STAGES) * STAGE_BYTES;
             const bool spread = SPREAD && ns < nk && !(ns == nk - 1 && krem < BK);
             if (ns < nk && !spread) issue_slab(ns, dst);
             read(kt + 1, na, nb);
@@ -482,7 +507,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                     }
         };
         if (nk > 0) {
-            if (nk >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
+            // slab 0 complete; slabs 1 .. PRO-1 may still be in flight
+            if (nk >= PRO) wait_vmcnt<(PRO - 1) * LOADS>();
             else wait_vmcnt<0>();
             __syncthreads();
             read(0, fa0, fb0);
