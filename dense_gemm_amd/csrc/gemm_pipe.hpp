@@ -292,14 +292,19 @@ struct PipeOperandS {
     __device__ __forceinline__ void issue(lds_char_t *lds, int wave)
     {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
-            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                         :
-                         : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
-                         : "memory");
-            ptr[i] += step;
-        }
+        for (int i = 0; i < LOADS; ++i) issue_one(lds, wave, i);
+    }
+
+    // Load i of this slab alone (the main loop spreads a slab's loads
+    // between its MFMAs).
+    __device__ __forceinline__ void issue_one(lds_char_t *lds, int wave, int i)
+    {
+        const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                     : "memory");
+        ptr[i] += step;
     }
 
     // The operand values of MFMA steps 4*c2 .. 4*c2+3 for block rows
@@ -528,12 +533,18 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * LOADS>();
             else wait_vmcnt<0>();
             __syncthreads();
-            if (kt + STAGES - 1 < nk) {
-                const int ns = (stage == 0 ? STAGES : stage) - 1;   // stage of slab kt-1
-                issue_slab(kt + STAGES - 1, smem + ns * STAGE_BYTES);
-            }
+            // slab kt+STAGES-1 goes into the stage of slab kt-1.  A regular
+            // slab's loads are spread between this slab's MFMAs (load l
+            // before MFMA l*NM/LOADS): a direct load stalls its SIMD's matrix
+            // core less there than in a burst after the barrier.  A partial
+            // last slab goes through registers, all at once.
+            const int ns = kt + STAGES - 1;
+            lds_char_t *dst = smem + ((stage == 0 ? STAGES : stage) - 1) * STAGE_BYTES;   // stage of slab kt-1
+            const bool spread = ns < nk && !(ns == nk - 1 && krem < BK);
+            if (ns < nk && !spread) issue_slab(ns, dst);
             const lds_char_t *sA = smem + stage * STAGE_BYTES;
             const lds_char_t *sB = sA + OpA::BYTES;
+            constexpr int NM = 2 * 4 * TM * TN;
             // 8 MFMA steps of k = 2 per slab, fragments 4 steps at a time
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
@@ -547,8 +558,17 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
-                        for (int j = 0; j < TN; ++j)
+                        for (int j = 0; j < TN; ++j) {
+                            const int m = ((c2 * 4 + e) * TM + i) * TN + j;
+#pragma unroll
+                            for (int l = 0; l < LOADS; ++l) {
+                                if (l * NM / LOADS == m && spread) {
+                                    if (l < OpA::LOADS) ga.issue_one(dst, wave, l);
+                                    else gb.issue_one(dst + OpA::BYTES, wave, l - OpA::LOADS);
+                                }
+                            }
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+                        }
             }
             stage = (stage + 1 == STAGES) ? 0 : stage + 1;
         }
