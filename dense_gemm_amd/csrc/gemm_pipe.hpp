@@ -478,16 +478,16 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 // reads must be complete in every wave
                 __syncthreads();
             }
-            // slab kt+PRO goes into the stage of slab kt-1 (LAG2) or kt.  With
-            // both operands k-contiguous (nt) a
-            // regular slab's loads are spread between this slab's MFMAs, load
-            // l before MFMA l*NM/LOADS: direct loads issued in a burst stall
-            // the matrix core of their SIMD more than the same loads
-            // interleaved with its MFMAs.  With a transposed-read operand
-            // (nn, tn) the spread loads slowed the kernel instead (measured
-            // 3-21%), so there they go in one burst.  A partial last slab
-            // goes through registers, all at once.
-            constexpr bool SPREAD = !TA && TB;
+            // slab kt+PRO goes into the stage of slab kt-1 (LAG2) or kt.  For
+            // nt, and for nn on tiles of at least 128 x 128, a regular slab's
+            // loads are spread between this slab's MFMAs, load l before MFMA
+            // l*NM/LOADS: direct loads issued in a burst stall the matrix core
+            // of their SIMD more than the same loads interleaved with its
+            // MFMAs (measured 1-8%).  tn (both operands through transposed
+            // reads) and nn on the narrow tiles measured slower spread (1-7%),
+            // so there they go in one burst.  A partial last slab goes
+            // through registers, all at once.
+            constexpr bool SPREAD = !TA && (TB || (BM >= 128 && BN >= 128));
             const int ns = kt + PRO;
             lds_char_t *dst = smem + (ns % STAGES) * STAGE_BYTES;
             const bool spread = SPREAD && ns < nk && !(ns == nk - 1 && krem < BK);
