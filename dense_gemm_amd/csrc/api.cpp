@@ -67,6 +67,8 @@ const Family kFamilies[] = {
     {"bf16_64x64_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE, dg::bf16_pipe_launchers, 3},
     {"bf16_128x32_pipe4_mfma32x32x16", DG_BF16_F32ACC, 128, 32, 4, PIPE, dg::bf16_pipe_launchers, 4},
     {"bf16_32x128_pipe4_mfma32x32x16", DG_BF16_F32ACC, 32, 128, 4, PIPE, dg::bf16_pipe_launchers, 5},
+    {"f16_256x256_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 256, 4, PIPE, dg::f16_pipe_launchers, 6},
+    {"bf16_256x256_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 256, 4, PIPE, dg::bf16_pipe_launchers, 6},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -74,7 +76,8 @@ enum {
     K_F16_PIPE_128 = 6, K_F16_PIPE_256 = 7, K_F16_PIPE_128_2 = 8, K_F32_PIPE_256x128 = 9,
     K_F32_PIPE_256x256 = 10, K_F32_PIPE_128 = 11, K_BF16_SIMPLE = 12, K_BF16_PIPE_128 = 13,
     K_BF16_PIPE_256 = 14, K_BF16_PIPE_128_2 = 15, K_F16_PIPE_64 = 16, K_F16_PIPE_128x32 = 17,
-    K_F16_PIPE_32x128 = 18, K_BF16_PIPE_64 = 19, K_BF16_PIPE_128x32 = 20, K_BF16_PIPE_32x128 = 21
+    K_F16_PIPE_32x128 = 18, K_BF16_PIPE_64 = 19, K_BF16_PIPE_128x32 = 20, K_BF16_PIPE_32x128 = 21,
+    K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -189,9 +192,7 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         if (pipe) return big >= 384 ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
-    // 16-bit operands: enough 256x128 tiles for two per CU: the big tile;
-    // enough 128x128 tiles for two per CU: the shallow two-workgroup
-    // pipeline; else the deep one-workgroup pipeline
+    // 16-bit operands: the tile is picked by how many CUs its tiles fill
     const bool bf = dtype == DG_BF16_F32ACC;
     if (pipe) {
         // narrow outputs take tiles that match them instead of padding a
@@ -203,8 +204,23 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // a single K slab: writing C dominates, the large tile fills the GPU
         // once there is one per CU (attention's Q K^T, measured)
         if (K <= 64 && big >= 256) return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
-        if (big >= 512) return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
-        if (small >= 512) return bf ? K_BF16_PIPE_128_2 : K_F16_PIPE_128_2;
+        // The tiles of one workgroup per CU run in waves of 256.  Once the
+        // 256x256 tiles fill more than half the CUs, the 256x128 tiles need
+        // two waves where the 256x256 tiles need one, and the 256x256 kernel
+        // does a tile's work at 15-30% less time per flop (measured 3072^3 to
+        // 8192^3 and 2304-4096 x 4096 x 512-16384: faster in every case but
+        // one tie at 6144^3 nt, where 2.25 waves round up against 4.5).
+        const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256) * nb;
+        if (t256 > 128) return bf ? K_BF16_PIPE_256x256 : K_F16_PIPE_256x256;
+        // 256x128 tiles on more than half the CUs: the 256x128 kernel, save
+        // for tn (both operands through transposed LDS reads), where the
+        // 128x128 kernel with two K groups was 13-16% faster (2048 x 3072-4096
+        // x 4096).  The two-workgroup 128x128 kernel measured slower than the
+        // one-workgroup one at every such shape and is not chosen.
+        if (big > 128) {
+            if (ta && !tb) return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
+            return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
+        }
         // fewer 128x128 tiles than half the CUs and K too short to split:
         // smaller tiles (the LoRA K = 32 products, measured)
         if (small < 128 && K < 1024) return bf ? K_BF16_PIPE_64 : K_F16_PIPE_64;

@@ -35,18 +35,20 @@ const launch_fn *f16_launchers(int config)
 //      attention's N = d_head products)
 //   4: 128x32 tile, 4 stages, four 32x32 waves (N = 32: low-rank products)
 //   5: 32x128 tile, 4 stages, four 32x32 waves (M = 32)
+//   6: 256x256 tile, 2 stages, eight 128x64 waves (large squares)
 #define DG_PIPE4(T, BM, BN, WM, WN, ST, KS)                                                   \
     {launch_pipe<T, BM, BN, WM, WN, false, false, ST, KS>, launch_pipe<T, BM, BN, WM, WN, false, true, ST, KS>, \
      launch_pipe<T, BM, BN, WM, WN, true, false, ST, KS>, launch_pipe<T, BM, BN, WM, WN, true, true, ST, KS>}
 const launch_fn *f16_pipe_launchers(int config)
 {
-    static const launch_fn table[6][4] = {
+    static const launch_fn table[7][4] = {
         DG_PIPE4(_Float16, 128, 128, 64, 64, 4, 2),
         DG_PIPE4(_Float16, 256, 128, 64, 64, 3, 1),
         DG_PIPE4(_Float16, 128, 128, 64, 64, 2, 2),
         DG_PIPE4(_Float16, 64, 64, 64, 32, 4, 2),
         DG_PIPE4(_Float16, 128, 32, 32, 32, 4, 1),
         DG_PIPE4(_Float16, 32, 128, 32, 32, 4, 1),
+        DG_PIPE4(_Float16, 256, 256, 128, 64, 2, 1),
     };
     return table[config];
 }

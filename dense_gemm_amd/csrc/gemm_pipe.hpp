@@ -421,7 +421,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     // consumed one step earlier.  The prologue issues the slabs the first
     // step does not issue itself.
     constexpr bool LAG2 = HALF && STAGES >= 4 && BM >= 128 && BN >= 128;
-    constexpr int PRO = (HALF && !LAG2) ? STAGES : STAGES - 1;
+    // 16-bit 256 x 256 tiles (eight 128 x 64 waves): fragments double-buffered
+    // per 16-wide k step instead of per slab (the slab-wide sets do not fit
+    // beside 128 accumulators), two stages, each step loading the next slab
+    // into the other stage; the prologue issues slab 0 only
+    constexpr bool FINE = HALF && BM == 256 && BN == 256;
+    static_assert(!FINE || (STAGES == 2 && KSPLIT == 1), "the 256 x 256 loop uses two stages");
+    constexpr int PRO = FINE ? 1 : ((HALF && !LAG2) ? STAGES : STAGES - 1);
 #pragma unroll
     for (int s = 0; s < PRO; ++s) {
         if (s < nk) issue_slab(s, smem + s * STAGE_BYTES);
@@ -437,7 +443,53 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 acc[i][j][r] = 0.f;
 
     constexpr int LOADS = OpA::LOADS + OpB::LOADS;
-    if constexpr (HALF) {
+    if constexpr (FINE) {
+        // Step kt: wait for slab kt (the only slab in flight), barrier (slab
+        // kt visible, every wave done with slab kt-1's stage), then the loads
+        // of slab kt+1 into that other stage, spread between this slab's
+        // MFMAs, and for each k step the next k step's fragments read one
+        // before each MFMA (order pinned by sched_barrier).
+        V8 fa[2][TM], fb[2][TN];
+        constexpr int NM = KPW * TM * TN;
+        for (int kt = 0; kt < nk; ++kt) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            const int ns = kt + 1;
+            lds_char_t *dst = smem + (ns % STAGES) * STAGE_BYTES;
+            const bool spread = ns < nk && !(ns == nk - 1 && krem < BK);
+            if (ns < nk && !spread) issue_slab(ns, dst);
+            const lds_char_t *sA = smem + (kt % STAGES) * STAGE_BYTES;
+            const lds_char_t *sB = sA + OpA::BYTES;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[0][i] = ga.frag(sA, wm0 + 32 * i, kk0, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[0][j] = gb.frag(sB, wn0 + 32 * j, kk0, lane);
+#pragma unroll
+            for (int s = 0; s < KPW; ++s) {
+                const int cur = s & 1, nxt = cur ^ 1;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int m = (s * TM + i) * TN + j;
+#pragma unroll
+                        for (int l = 0; l < LOADS; ++l) {
+                            if (l * NM / LOADS == m && spread) {
+                                if (l < OpA::LOADS) ga.issue_one(dst, wave, l);
+                                else gb.issue_one(dst + OpA::BYTES, wave, l - OpA::LOADS);
+                            }
+                        }
+                        const int f = i * TN + j;        // fragment of the next k step
+                        if (s + 1 < KPW) {
+                            if (f < TM) fa[nxt][f] = ga.frag(sA, wm0 + 32 * f, kk0 + s + 1, lane);
+                            else if (f < TM + TN) fb[nxt][f - TM] = gb.frag(sB, wn0 + 32 * (f - TM), kk0 + s + 1, lane);
+                        }
+                        acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
+        }
+    } else if constexpr (HALF) {
         // Two fragment sets, the loop unrolled by two so that each set stays
         // in fixed registers.  The next slab's LDS reads are unconditional:
         // after the last slab they read a stale stage that is never used, so

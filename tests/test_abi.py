@@ -122,6 +122,8 @@ def test_selection_picks_matrix_core_kernels_of_the_right_type():
     # the headline shapes get the large tiles
     k = dg.dg_select_kernel(0, 0, 4096, 4096, 4096, NULL, 4096, NULL, 4096, NULL, 4096, 0)
     assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 128)
+    k = dg.dg_select_kernel(0, 0, 4096, 4096, 4096, NULL, 4096, NULL, 4096, NULL, 4096, 1)
+    assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 256)
     k = dg.dg_select_kernel(0, 0, 2048, 2048, 2048, NULL, 2048, NULL, 2048, NULL, 2048, 1)
     assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (128, 128)
 
@@ -144,6 +146,29 @@ def test_underfilled_16bit_grids_take_64x64_tiles_unsplit():
     assert tile_of(512, 5632, 2048) == (128, 128)
     # fp32 is not affected
     assert tile_of(512, 2048, 5632, 0) != (64, 64)
+
+
+def test_16bit_large_grids_take_the_tile_that_fills_the_cus_in_one_wave():
+    for dtype in (1, 2):
+        # more than 128 tiles of 256x256: the 256x256 kernel, every transpose pair
+        for M, N, K in ((4096, 4096, 4096), (3072, 3072, 3072), (8192, 8192, 1024), (2304, 4096, 2048),
+                        (6144, 6144, 6144)):
+            for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+                k = dg.dg_select_kernel(ta, tb, M, N, K, 256, M if ta else K, 256, K if tb else N, 256, N,
+                                        dtype)
+                assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 256), (M, N, K, ta, tb)
+        # 129-256 tiles of 256x128: 256x128 except tn, which keeps 128x128
+        for M, N, K in ((2048, 4096, 4096), (2560, 2560, 4096), (8192, 1024, 1024)):
+            assert tile_of(M, N, K, dtype) == (256, 128), (M, N, K)
+            k = dg.dg_select_kernel(1, 0, M, N, K, 256, M, 256, N, 256, N, dtype)
+            assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (128, 128), (M, N, K)
+        # at most 128 such tiles: 128x128
+        assert tile_of(2048, 2048, 2048, dtype) == (128, 128)
+        assert tile_of(2048, 2048, 8192, dtype) == (128, 128)
+        # the two-workgroup 128x128 kernel is never chosen
+        for M, N, K in ((2048, 4096, 1024), (3072, 3072, 3072), (4096, 4096, 512)):
+            k = dg.dg_select_kernel(0, 0, M, N, K, 256, K, 256, N, 256, N, dtype)
+            assert "pipe2_ksplit2" not in dg.dg_kernel_name(k)
 
 
 def test_tile_grid_matches_the_pages_decompositions():
@@ -260,5 +285,5 @@ def test_ex_forced_kernel_checks():
 def test_bf16_kernels_listed():
     names = dg.kernel_names()
     for n in ("bf16_64x64_simple", "bf16_128x128_pipe4_ksplit2_mfma32x32x16",
-              "bf16_256x128_pipe3_w8_mfma32x32x16"):
+              "bf16_256x128_pipe3_w8_mfma32x32x16", "bf16_256x256_pipe2_w8_mfma32x32x16"):
         assert n in names
