@@ -172,7 +172,11 @@ bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int
 {
     const int64_t v = 16 / elem_bytes(dtype);
     (void)K;
-    return vec_ok(A, lda, B, ldb, dtype, x) && (!ta || M % v == 0) && (tb || N % v == 0);
+    // the direct loads address a tile panel with 32-bit byte offsets, at most
+    // 256 rows of the stored matrix from the panel's origin
+    const int64_t lim = (int64_t)1 << 31;
+    const bool offsets_fit = 256 * lda * elem_bytes(dtype) < lim && 256 * ldb * elem_bytes(dtype) < lim;
+    return offsets_fit && vec_ok(A, lda, B, ldb, dtype, x) && (!ta || M % v == 0) && (tb || N % v == 0);
 }
 
 // Kernel choice by dtype, preconditions and output tile count.  Larger tiles

@@ -15,8 +15,13 @@
 // compute unit leaves a single wave per SIMD, and one 64-wide K slab is only
 // ~512 MFMA cycles, shorter than a load round trip.  So the slabs are
 // prefetched STAGES-1 deep, and the loads go straight to LDS
-// (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane),
-// which costs no registers and no transposing VALU work.
+// (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at M0 + 16*lane),
+// which costs no registers and no transposing VALU work.  The buffer form
+// addresses each lane with a 32-bit offset from a wave-uniform base held in
+// scalar registers; beside the MFMAs it measured about half the matrix-core
+// stall of the global form, whose 64-bit per-lane addresses the SIMD sends
+// to the address unit (a microbenchmark of one GEMM slab per iteration: 615
+// cycles against 720, with 475 for the MFMAs alone and 500 for the loads).
 //
 // fp16 LDS layouts (both conflict-free for the fragment reads):
 //   k-contiguous operand (A not transposed, B transposed): [BMN][64] halfs,
@@ -78,6 +83,37 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int PIPE_BK = 64;
 
+// Buffer resource of a raw byte buffer at `base` (gfx9 layout: 48-bit base,
+// stride 0, num_records, format dword).  num_records is the largest value:
+// the kernels bound every offset themselves (rows clamped to the matrix), as
+// the global form did.  The fields are made wave-uniform so that the
+// resource lives in scalar registers, as the instruction requires.
+typedef int i32x4_rsrc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_rsrc buffer_rsrc(const char *base)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    i32x4_rsrc r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff);
+    r[2] = -1;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// One direct load: 16 bytes per lane from base + voff into LDS at
+// lds_addr + 16 * lane.  Inline asm, so that the compiler does not track it:
+// it would otherwise wait for every direct load in flight (all prefetched
+// slabs) before each LDS read and barrier.  Completion is awaited explicitly
+// with wait_vmcnt (vector-memory loads retire in order).  M0 holds the
+// wave-uniform LDS destination.
+__device__ __forceinline__ void load_lds16(uint32_t voff, i32x4_rsrc rsrc, unsigned lds_addr)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory");
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 template <int N>
@@ -108,14 +144,17 @@ struct PipeOperandH {
         return QUADS >= 4 ? (k & 3) : (QUADS == 2 ? ((k >> 1) & 1) : 0);
     }
 
-    const E *ptr[LOADS];         // per-lane global addresses of the current slab
-    int64_t step;                // elements to advance per slab
+    const char *base;            // the current slab's tile origin (wave-uniform)
+    uint32_t off[LOADS];         // per-lane byte offsets from base
+    int64_t step;                // bytes to advance per slab
 
-    // Per-lane addresses for the slab at k = 0.  mn0: first row (m or n) of
-    // the tile; ext: M or N; ld: row stride of the stored matrix.
+    // Per-lane offsets for the slab at k = 0.  mn0: first row (m or n) of
+    // the tile; ext: M or N; ld: row stride of the stored matrix.  Offsets
+    // stay below 256 * ld * 2 bytes (the dispatcher keeps that under 2^31).
     __device__ __forceinline__ void init(const E *g, int64_t ld, int mn0, int ext, int wave,
                                          int lane)
     {
+        base = (const char *)(KCONT ? g + (int64_t)mn0 * ld : g + mn0);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int rbase = (i * NW + wave) * ROWS_PER_LOAD;  // first LDS row of this load
@@ -124,18 +163,20 @@ struct PipeOperandH {
                 const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical 16-byte chunk (8 k)
                 int row = mn0 + r;
                 row = row < ext ? row : ext - 1;
-                ptr[i] = g + (int64_t)row * ld + c * 8;
+                off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 8) * 2);
             } else {
                 const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
                 const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
                 const int q = (p >> 2) ^ swz(r);                  // logical 64-byte quad
                 int col = mn0 + q * 32 + (p & 3) * 8;
                 col = col < ext ? col : ext - 8;
-                ptr[i] = g + (int64_t)r * ld + col;
+                off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 2);
             }
         }
-        step = KCONT ? PIPE_BK : PIPE_BK * ld;
+        step = (KCONT ? PIPE_BK : PIPE_BK * ld) * 2;
     }
+
+    __device__ __forceinline__ void advance() { base += step; }
 
     // The last slab when K is not a multiple of 64: the same 16-byte pieces
     // into the same LDS slots, but through registers, with k at or beyond K
@@ -154,45 +195,36 @@ struct PipeOperandH {
                 const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
                 valid = r < krem ? 8 : 0;
             }
+            const E *src = (const E *)(base + off[i]);
             V8 v;
             if (valid >= 8) {
-                v = *(const V8 *)ptr[i];
+                v = *(const V8 *)src;
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     E x = (E)0.f;
-                    if (e < valid) x = ptr[i][e];
+                    if (e < valid) x = src[e];
                     v[e] = x;
                 }
             }
             *(lds_v8_t *)dst = v;
-            ptr[i] += step;
         }
+        advance();
     }
 
     // Issue this slab's direct loads into the stage at `lds` and advance.
-    // The load is written as inline asm so that the compiler does not track
-    // it: it would otherwise wait for every direct load in flight (all
-    // prefetched slabs) before each LDS read and barrier.  Completion is
-    // instead awaited explicitly with wait_vmcnt (vector-memory loads retire
-    // in order).  M0 holds the wave-uniform LDS destination; each lane's 16
-    // bytes land at M0 + 16 * lane.
     __device__ __forceinline__ void issue(lds_char_t *lds, int wave)
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) issue_one(lds, wave, i);
+        advance();
     }
 
     // Load i of this slab alone (the main loop spreads a slab's loads
-    // between its MFMAs).
+    // between its MFMAs and calls advance() after the last one).
     __device__ __forceinline__ void issue_one(lds_char_t *lds, int wave, int i)
     {
-        const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
-                     : "memory");
-        ptr[i] += step;
+        load_lds16(off[i], buffer_rsrc(base), (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024));
     }
 
     // MFMA operand of block rows [b0, b0+32) for k-step kk (16 k) of a stage.
@@ -232,12 +264,15 @@ struct PipeOperandS {
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
     static_assert(ROWS_PER_LOAD >= 1, "rows of at most 1 KiB");
 
-    const float *ptr[LOADS];
-    int64_t step;
+    const char *base;            // the current slab's tile origin (wave-uniform)
+    uint32_t off[LOADS];         // per-lane byte offsets from base
+    int64_t step;                // bytes to advance per slab
 
+    // As the 16-bit operand; offsets stay below 256 * ld * 4 bytes.
     __device__ __forceinline__ void init(const float *g, int64_t ld, int mn0, int ext, int wave,
                                          int lane)
     {
+        base = (const char *)(KCONT ? g + (int64_t)mn0 * ld : g + mn0);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int rbase = (i * NW + wave) * ROWS_PER_LOAD;
@@ -246,18 +281,20 @@ struct PipeOperandS {
                 const int c = (lane & 3) ^ ((r >> 2) & 3);    // logical 16-byte chunk (4 k)
                 int row = mn0 + r;
                 row = row < ext ? row : ext - 1;
-                ptr[i] = g + (int64_t)row * ld + c * 4;
+                off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4) * 4);
             } else {
                 const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
                 const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
                 const int q = (p >> 3) ^ ((r >> 3) & 1);          // logical 128-byte chunk
                 int col = mn0 + q * 32 + (p & 7) * 4;
                 col = col < ext ? col : ext - 4;
-                ptr[i] = g + (int64_t)r * ld + col;
+                off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
             }
         }
-        step = KCONT ? BK : BK * ld;
+        step = (KCONT ? BK : BK * ld) * 4;
     }
+
+    __device__ __forceinline__ void advance() { base += step; }
 
     __device__ __forceinline__ void issue_tail(lds_char_t *lds, int wave, int lane, int krem)
     {
@@ -273,38 +310,35 @@ struct PipeOperandS {
                 const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
                 valid = r < krem ? 4 : 0;
             }
+            const float *src = (const float *)(base + off[i]);
             f32x4 v;
             if (valid >= 4) {
-                v = *(const f32x4 *)ptr[i];
+                v = *(const f32x4 *)src;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float x = 0.f;
-                    if (e < valid) x = ptr[i][e];
+                    if (e < valid) x = src[e];
                     v[e] = x;
                 }
             }
             *(__attribute__((address_space(3))) f32x4 *)dst = v;
-            ptr[i] += step;
         }
+        advance();
     }
 
     __device__ __forceinline__ void issue(lds_char_t *lds, int wave)
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) issue_one(lds, wave, i);
+        advance();
     }
 
     // Load i of this slab alone (the main loop spreads a slab's loads
-    // between its MFMAs).
+    // between its MFMAs and calls advance() after the last one).
     __device__ __forceinline__ void issue_one(lds_char_t *lds, int wave, int i)
     {
-        const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024);
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(ptr[i]), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
-                     : "memory");
-        ptr[i] += step;
+        load_lds16(off[i], buffer_rsrc(base), (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024));
     }
 
     // The operand values of MFMA steps 4*c2 .. 4*c2+3 for block rows
@@ -488,6 +522,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                         __builtin_amdgcn_sched_barrier(0);
                     }
             }
+            if (spread) {
+                ga.advance();
+                gb.advance();
+            }
         }
     } else if constexpr (HALF) {
         // Two fragment sets, the loop unrolled by two so that each set stays
@@ -580,6 +618,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                         acc[i][j] = mfma_32x32x16(ca[s][i], cb[s][j], acc[i][j]);
                         if constexpr (SPLITRD) __builtin_amdgcn_sched_barrier(0);
                     }
+            if (spread) {
+                ga.advance();
+                gb.advance();
+            }
         };
         if (nk > 0) {
             // slab 0 complete; slabs 1 .. PRO-1 may still be in flight
@@ -639,6 +681,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                             }
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
                         }
+            }
+            if (spread) {
+                ga.advance();
+                gb.advance();
             }
             stage = (stage + 1 == STAGES) ? 0 : stage + 1;
         }
