@@ -171,6 +171,19 @@ def test_16bit_large_grids_take_the_tile_that_fills_the_cus_in_one_wave():
             assert "pipe2_ksplit2" not in dg.dg_kernel_name(k)
 
 
+def test_pipelined_kernels_need_32bit_panel_offsets():
+    # a tile panel is addressed with 32-bit byte offsets: 256 rows of the
+    # stored matrix must span less than 2^31 bytes, else the register-staged
+    # kernels take the problem
+    for dtype, esize in ((0, 4), (1, 2), (2, 2)):
+        big = (1 << 31) // (256 * esize)          # the first row stride that does not fit
+        for ld, pipe in ((big - 64, True), (big, False)):
+            k = dg.dg_select_kernel(0, 0, 512, 512, 512, 256, ld, 256, 512, 256, 512, dtype)
+            assert ("pipe" in dg.dg_kernel_name(k)) == pipe, (dtype, ld, dg.dg_kernel_name(k))
+            k = dg.dg_select_kernel(0, 0, 512, 512, 512, 256, 512, 256, ld, 256, 512, dtype)
+            assert ("pipe" in dg.dg_kernel_name(k)) == pipe, (dtype, ld, dg.dg_kernel_name(k))
+
+
 def test_tile_grid_matches_the_pages_decompositions():
     """Output tiles of side T cover C[35,93] at ((35//T)*T, (93//T)*T): the
     8x8 tile at (32,88) entry (3,5) and the 64x64 tile at (0,64) of the pages
