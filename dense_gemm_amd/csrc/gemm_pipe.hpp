@@ -569,15 +569,16 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 __syncthreads();
             }
             // slab kt+PRO goes into the stage of slab kt-1 (LAG2) or kt.  For
-            // nt, and for nn on tiles of at least 128 x 128, a regular slab's
-            // loads are spread between this slab's MFMAs, load l before MFMA
+            // nn and nt on tiles of at least 128 x 128, a regular slab's loads
+            // are spread between this slab's MFMAs, load l before MFMA
             // l*NM/LOADS: direct loads issued in a burst stall the matrix core
             // of their SIMD more than the same loads interleaved with its
             // MFMAs (measured 1-8%).  tn (both operands through transposed
-            // reads) and nn on the narrow tiles measured slower spread (1-7%),
-            // so there they go in one burst.  A partial last slab goes
-            // through registers, all at once.
-            constexpr bool SPREAD = !TA && (TB || (BM >= 128 && BN >= 128));
+            // reads) measured 3.5-6% slower spread, and the narrow tiles
+            // 9-16% slower for nt (no difference for nn), so there the loads
+            // go in one burst.  A partial last slab goes through registers,
+            // all at once.
+            constexpr bool SPREAD = !TA && BM >= 128 && BN >= 128;
             const int ns = kt + PRO;
             lds_char_t *dst = smem + (ns % STAGES) * STAGE_BYTES;
             const bool spread = SPREAD && ns < nk && !(ns == nk - 1 && krem < BK);
