@@ -90,3 +90,37 @@ def test_splitk_very_long_k(dg, dtype):
     ref, ab = oracle.gemm(False, False, M, N, K, 0.5, a, K, b, N, -1.0, c0, N)
     worst, bad = oracle.compare(dtype, C.float().cpu().numpy(), ref, ab, 0.5, -1.0, c0)
     assert bad == 0, worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_panel_offsets_near_2_pow_31(dg, dtype):
+    """A (k-contiguous) with the largest row stride the pipelined kernels
+    take: 256 rows of it span just under 2^31 bytes, so the direct loads'
+    32-bit byte offsets of the last row come within 1/256 of 2^31.  Only the
+    logical K columns of each row are written; every output is compared with
+    the oracle."""
+    import torch
+    dev = torch.device("cuda:0")
+    esize = 4 if dtype == "f32" else 2
+    lda = (1 << 31) // (256 * esize) - 64
+    M, N, K = 256, 128, 64
+    assert 255 * lda * esize > (1 << 31) - (1 << 24)
+    a, b, _ = synth.problem(M, N, K, dtype, "uniform" if dtype == "f32" else "normal_sqrtk", 530)
+    tdt = torch.float32 if dtype == "f32" else torch.float16
+    code = dg.DG_F32 if dtype == "f32" else dg.DG_F16_F32ACC
+    At = torch.empty((M, lda), dtype=tdt, device=dev)
+    At[:, :K] = torch.from_numpy(a).to(dev)
+    Bt = torch.from_numpy(b).to(dev)
+    Ct = torch.full((M, N), float("nan"), dtype=tdt, device=dev)
+    k = dg.dg_select_kernel(0, 0, M, N, K, At.data_ptr(), lda, Bt.data_ptr(), N, Ct.data_ptr(), N, code)
+    assert "pipe" in dg.dg_kernel_name(k), dg.dg_kernel_name(k)
+    print(f"panel offsets near 2^31: {dtype} lda={lda} kernel={dg.dg_kernel_name(k)}", flush=True)
+    rc = dg.dg_gemm(0, 0, M, N, K, 1.0, At.data_ptr(), lda, Bt.data_ptr(), N, 0.0, Ct.data_ptr(), N,
+                    code, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, dg.dg_status_string(rc)
+    torch.cuda.synchronize()
+    got = Ct.float().cpu().numpy()
+    del At
+    ref, ab = oracle.gemm(False, False, M, N, K, 1.0, a, K, b, N, 0.0, None, N)
+    worst, bad = oracle.compare(dtype, got, ref, ab, 1.0, 0.0)
+    assert bad == 0, worst
