@@ -492,6 +492,6 @@ const char *dg_status_string(int status)
 
 int dg_last_hip_error(void) { return g_last_hip_error; }
 
-int dg_version(void) { return 200; }
+int dg_version(void) { return 300; }
 
 }  // extern "C"

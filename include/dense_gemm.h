@@ -96,7 +96,10 @@ int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha
  * kernel table, see dg_kernel_count / dg_kernel_name) instead of the one the
  * library would pick; DG_KERNEL_AUTO behaves as dg_gemm.  Returns
  * DG_ERR_UNSUPPORTED (nothing enqueued) when that kernel does not handle the
- * problem's dtype, transposes or alignment.  For tests and measurement. */
+ * problem's dtype, transposes, alignment or row strides (the pipelined
+ * kernels address a tile's operands with 32-bit byte offsets, so they need
+ * 256 rows of the stored A and of the stored B to span less than 2^31
+ * bytes).  For tests and measurement. */
 int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
                         void *C, int64_t ldc, int dtype, void *stream, int kernel);
