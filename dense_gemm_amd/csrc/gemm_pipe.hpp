@@ -457,8 +457,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     constexpr bool LAG2 = HALF && STAGES >= 4 && BM >= 128 && BN >= 128;
     // 16-bit 256 x 256 tiles (eight 128 x 64 waves): fragments double-buffered
     // per 16-wide k step instead of per slab (the slab-wide sets do not fit
-    // beside 128 accumulators), two stages, each step loading the next slab
-    // into the other stage; the prologue issues slab 0 only
+    // beside 128 accumulators), two stages; the prologue issues slab 0 only
     constexpr bool FINE = HALF && BM == 256 && BN == 256;
     static_assert(!FINE || (STAGES == 2 && KSPLIT == 1), "the 256 x 256 loop uses two stages");
     constexpr int PRO = FINE ? 1 : ((HALF && !LAG2) ? STAGES : STAGES - 1);
@@ -478,50 +477,70 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
 
     constexpr int LOADS = OpA::LOADS + OpB::LOADS;
     if constexpr (FINE) {
-        // Step kt: wait for slab kt (the only slab in flight), barrier (slab
-        // kt visible, every wave done with slab kt-1's stage), then the loads
-        // of slab kt+1 into that other stage, spread between this slab's
-        // MFMAs, and for each k step the next k step's fragments read one
-        // before each MFMA (order pinned by sched_barrier).
+        // Slab kt: k steps 0..KPW-2 run from registers, each reading the next
+        // k step's fragments one before each MFMA (order pinned by
+        // sched_barrier).  Then this wave waits for its loads of slab kt+1
+        // and its fragment reads, and the workgroup meets at a barrier: slab
+        // kt+1 is visible, and every wave is done with slab kt's stage.  The
+        // last k step then runs while slab kt+1's first fragments are read
+        // and slab kt+2 is loaded into slab kt's stage, one load before each
+        // MFMA.  So no fragment read waits at a barrier, and each load has
+        // KPW-1 k steps of the next slab to land.  The reads after the last
+        // slab fetch a stale stage that is never used (no branch between
+        // them and the MFMAs).
         V8 fa[2][TM], fb[2][TN];
-        constexpr int NM = KPW * TM * TN;
+        constexpr int NL = TM * TN;              // MFMAs of one k step
+        static_assert(KPW % 2 == 0, "k steps alternate between the two fragment sets");
+        wait_vmcnt<0>();
+        __syncthreads();                         // slab 0 visible
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[0][i] = ga.frag(smem, wm0 + 32 * i, kk0, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[0][j] = gb.frag(smem + OpA::BYTES, wn0 + 32 * j, kk0, lane);
+        if (nk > 1) issue_slab(1, smem + STAGE_BYTES);
         for (int kt = 0; kt < nk; ++kt) {
-            wait_vmcnt<0>();
-            __syncthreads();
-            const int ns = kt + 1;
-            lds_char_t *dst = smem + (ns % STAGES) * STAGE_BYTES;
-            const bool spread = ns < nk && !(ns == nk - 1 && krem < BK);
-            if (ns < nk && !spread) issue_slab(ns, dst);
             const lds_char_t *sA = smem + (kt % STAGES) * STAGE_BYTES;
             const lds_char_t *sB = sA + OpA::BYTES;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[0][i] = ga.frag(sA, wm0 + 32 * i, kk0, lane);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb[0][j] = gb.frag(sB, wn0 + 32 * j, kk0, lane);
-#pragma unroll
-            for (int s = 0; s < KPW; ++s) {
+            for (int s = 0; s + 1 < KPW; ++s) {
                 const int cur = s & 1, nxt = cur ^ 1;
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j) {
-                        const int m = (s * TM + i) * TN + j;
-#pragma unroll
-                        for (int l = 0; l < LOADS; ++l) {
-                            if (l * NM / LOADS == m && spread) {
-                                if (l < OpA::LOADS) ga.issue_one(dst, wave, l);
-                                else gb.issue_one(dst + OpA::BYTES, wave, l - OpA::LOADS);
-                            }
-                        }
                         const int f = i * TN + j;        // fragment of the next k step
-                        if (s + 1 < KPW) {
-                            if (f < TM) fa[nxt][f] = ga.frag(sA, wm0 + 32 * f, kk0 + s + 1, lane);
-                            else if (f < TM + TN) fb[nxt][f - TM] = gb.frag(sB, wn0 + 32 * (f - TM), kk0 + s + 1, lane);
-                        }
+                        if (f < TM) fa[nxt][f] = ga.frag(sA, wm0 + 32 * f, kk0 + s + 1, lane);
+                        else if (f < TM + TN) fb[nxt][f - TM] = gb.frag(sB, wn0 + 32 * (f - TM), kk0 + s + 1, lane);
                         acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
             }
+            wait_vmcnt<0>();
+            __syncthreads();
+            const int n2 = kt + 2;
+            lds_char_t *dst = smem + (kt % STAGES) * STAGE_BYTES;   // slab n2's stage (two stages)
+            const lds_char_t *rA = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
+            const lds_char_t *rB = rA + OpA::BYTES;
+            const bool spread = n2 < nk && !(n2 == nk - 1 && krem < BK);
+            if (n2 < nk && !spread) issue_slab(n2, dst);
+            constexpr int cur = (KPW - 1) & 1, nxt = cur ^ 1;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int m = i * TN + j;
+#pragma unroll
+                    for (int l = 0; l < LOADS; ++l) {
+                        if (l * NL / LOADS == m && spread) {
+                            if (l < OpA::LOADS) ga.issue_one(dst, wave, l);
+                            else gb.issue_one(dst + OpA::BYTES, wave, l - OpA::LOADS);
+                        }
+                    }
+                    if (m < TM) fa[nxt][m] = ga.frag(rA, wm0 + 32 * m, kk0, lane);
+                    else if (m < TM + TN) fb[nxt][m - TM] = gb.frag(rB, wn0 + 32 * (m - TM), kk0, lane);
+                    acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             if (spread) {
                 ga.advance();
                 gb.advance();
