@@ -372,6 +372,34 @@ def epilogue_cost(dev, stream, reps):
     return res
 
 
+def smi_clocks(index=0):
+    """Clock state from `amd-smi metric --clock --json` (a child process): the
+    median current shader clock over the XCDs, its range, whether it is
+    locked, and the memory clock.  None when the tool is missing or fails.
+    The tool starts in about a second, so it sees the GPU idle between
+    launches; the clock under load is the control probe's."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout)
+        gpus = data["gpu_data"] if isinstance(data, dict) else data
+        clk = next(g for g in gpus if g.get("gpu") == index)["clock"]
+
+        def val(x):
+            return x["value"] if isinstance(x, dict) else None
+
+        gfx = [val(v["clk"]) for k, v in clk.items() if k.startswith("gfx_")]
+        gfx = sorted(x for x in gfx if x is not None)
+        g0 = clk.get("gfx_0", {})
+        mem = clk.get("mem_0", {})
+        return {"gfx_mhz_median": gfx[len(gfx) // 2] if gfx else None,
+                "gfx_min_mhz": val(g0.get("min_clk")), "gfx_max_mhz": val(g0.get("max_clk")),
+                "gfx_locked": g0.get("clk_locked"), "mem_mhz": val(mem.get("clk"))}
+    except Exception:
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +433,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
+    smi_before = smi_clocks()
     control = control_probes(dev, stream)
 
     if args.copy_calibration:
@@ -443,6 +472,7 @@ def main():
     f32_launches = per_launch(step, stream, 20)
     scrub = None if args.no_cold else torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
     f32_cold_us = None if args.no_cold else cold_launches(step, stream, 5, scrub)   # 512 MiB scrub
+    smi_after = smi_clocks()
 
     out = {
         "metric": "TFLOP/s + % of MFMA peak: fp32 4096^3 nn; fp16->fp32 2048^3 nn/tn/nt",
@@ -468,6 +498,7 @@ def main():
         "per_launch_us": f32_launches,
         "cold_us": f32_cold_us,
         "control": control,
+        "smi_clocks": {"before": smi_before, "after_fp32": smi_after},
     }
     if not control["within_tolerance"]:
         out["gate"] = ("a control benchmark is more than 10% from its reference: "
