@@ -33,7 +33,10 @@ thread_local int g_last_hip_error = 0;
 //   PIPE:   direct-to-LDS pipelined kernels; 4 variants (transA x transB);
 //           need 16-byte aligned rows of A and B, and the m/n-contiguous
 //           operand's extent a multiple of 16 bytes.
-enum Kind { SIMPLE, MFMA, PIPE };
+//   PIPE_DW: fp32 pipelined kernels with 4-byte direct loads; any fp32
+//           layout (4-byte aligned A and B).
+//   Both pipelined kinds address a tile's operands with 32-bit byte offsets.
+enum Kind { SIMPLE, MFMA, PIPE, PIPE_DW };
 struct Family {
     const char *name;
     int dtype;
@@ -69,6 +72,8 @@ const Family kFamilies[] = {
     {"bf16_32x128_pipe4_mfma32x32x16", DG_BF16_F32ACC, 32, 128, 4, PIPE, dg::bf16_pipe_launchers, 5},
     {"f16_256x256_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 256, 4, PIPE, dg::f16_pipe_launchers, 6},
     {"bf16_256x256_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 256, 4, PIPE, dg::bf16_pipe_launchers, 6},
+    {"f32_256x128_pipe3_dw_mfma32x32x2", DG_F32, 256, 128, 8, PIPE_DW, dg::f32_pipe_launchers, 3},
+    {"f32_128x128_pipe4_dw_mfma32x32x2", DG_F32, 128, 128, 8, PIPE_DW, dg::f32_pipe_launchers, 4},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -77,7 +82,8 @@ enum {
     K_F32_PIPE_256x256 = 10, K_F32_PIPE_128 = 11, K_BF16_SIMPLE = 12, K_BF16_PIPE_128 = 13,
     K_BF16_PIPE_256 = 14, K_BF16_PIPE_128_2 = 15, K_F16_PIPE_64 = 16, K_F16_PIPE_128x32 = 17,
     K_F16_PIPE_32x128 = 18, K_BF16_PIPE_64 = 19, K_BF16_PIPE_128x32 = 20, K_BF16_PIPE_32x128 = 21,
-    K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23
+    K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23, K_F32_PIPE_256x128_DW = 24,
+    K_F32_PIPE_128_DW = 25
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -164,6 +170,14 @@ bool vec_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype, c
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The direct loads address a tile panel with 32-bit byte offsets, at most
+// 256 rows of the stored matrix from the panel's origin.
+bool offsets_fit(int64_t lda, int64_t ldb, int dtype)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    return 256 * lda * elem_bytes(dtype) < lim && 256 * ldb * elem_bytes(dtype) < lim;
+}
+
 // Preconditions of the pipelined kernels (see Family): 16-byte aligned rows
 // of A and B, and the m/n-contiguous operand's extent a whole number of
 // 16-byte pieces.
@@ -172,11 +186,16 @@ bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int
 {
     const int64_t v = 16 / elem_bytes(dtype);
     (void)K;
-    // the direct loads address a tile panel with 32-bit byte offsets, at most
-    // 256 rows of the stored matrix from the panel's origin
-    const int64_t lim = (int64_t)1 << 31;
-    const bool offsets_fit = 256 * lda * elem_bytes(dtype) < lim && 256 * ldb * elem_bytes(dtype) < lim;
-    return offsets_fit && vec_ok(A, lda, B, ldb, dtype, x) && (!ta || M % v == 0) && (tb || N % v == 0);
+    return offsets_fit(lda, ldb, dtype) && vec_ok(A, lda, B, ldb, dtype, x) && (!ta || M % v == 0) &&
+           (tb || N % v == 0);
+}
+
+// Preconditions of the fp32 pipelined kernels with 4-byte loads: 4-byte
+// aligned A and B (any row stride and extent).
+bool pipe_dw_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype)
+{
+    return dtype == DG_F32 && ((uintptr_t)A & 3) == 0 && ((uintptr_t)B & 3) == 0 &&
+           offsets_fit(lda, ldb, dtype);
 }
 
 // Kernel choice by dtype, preconditions and output tile count.  Larger tiles
@@ -194,6 +213,9 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // measured the same on average over four boxes (each ahead on some:
         // the spread follows the boxes' clocks, 2.16-2.40 GHz under load)
         if (pipe) return big >= 384 ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
+        // rows not 16-byte aligned: the same kernels with 4-byte direct loads
+        if (pipe_dw_ok(A, lda, B, ldb, dtype))
+            return big >= 384 ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
     // 16-bit operands: the tile is picked by how many CUs its tiles fill
@@ -251,6 +273,7 @@ bool supports(int kernel, int ta, int tb, int64_t M, int64_t N, int64_t K, const
     if (f.dtype != dtype) return false;
     if (f.kind == SIMPLE) return ceil_div(M, 64) <= 65535;
     if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x)) return false;
+    if (f.kind == PIPE_DW && !pipe_dw_ok(A, lda, B, ldb, dtype)) return false;
     return ceil_div(M, f.bm) * ceil_div(N, f.bn) <= 0x7fffffff;
 }
 
@@ -333,7 +356,7 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
                     p.k_chunk = 0;
                 }
             }
-            const int vi = (f.kind == PIPE || vec_ok(A, lda, B, ldb, dtype, x)) ? 0 : 4;
+            const int vi = (f.kind == PIPE || f.kind == PIPE_DW || vec_ok(A, lda, B, ldb, dtype, x)) ? 0 : 4;
             err = f.variants(f.config)[vi + ta * 2 + tb](p, s);
             if (err == hipSuccess && p.splits > 1) err = dg::splitk_reduce_launcher(di)(p, s);
         }

@@ -30,17 +30,24 @@ const launch_fn *f32_launchers(int config)
 //   0: 256x128 tile, 3 stages, 4 waves of 128x64 (two workgroups per CU)
 //   1: 256x256 tile, 4 stages, 8 waves of 128x64 (one workgroup per CU)
 //   2: 128x128 tile, 4 stages, 4 waves of 64x64 (two workgroups per CU)
+//   3, 4: configs 0 and 2 with 4-byte direct loads (rows not 16-byte aligned)
+#define DG_PIPE4DW(BM, BN, WM, WN, ST)                                                              \
+    {launch_pipe<float, BM, BN, WM, WN, false, false, ST, 1, 4>, launch_pipe<float, BM, BN, WM, WN, false, true, ST, 1, 4>, \
+     launch_pipe<float, BM, BN, WM, WN, true, false, ST, 1, 4>, launch_pipe<float, BM, BN, WM, WN, true, true, ST, 1, 4>}
 const launch_fn *f32_pipe_launchers(int config)
 {
-    static const launch_fn table[3][4] = {
+    static const launch_fn table[5][4] = {
         {launch_pipe<float, 256, 128, 128, 64, false, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, false, true, 3, 1>,
          launch_pipe<float, 256, 128, 128, 64, true, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, true, true, 3, 1>},
         {launch_pipe<float, 256, 256, 128, 64, false, false, 4, 1>, launch_pipe<float, 256, 256, 128, 64, false, true, 4, 1>,
          launch_pipe<float, 256, 256, 128, 64, true, false, 4, 1>, launch_pipe<float, 256, 256, 128, 64, true, true, 4, 1>},
         {launch_pipe<float, 128, 128, 64, 64, false, false, 4, 1>, launch_pipe<float, 128, 128, 64, 64, false, true, 4, 1>,
          launch_pipe<float, 128, 128, 64, 64, true, false, 4, 1>, launch_pipe<float, 128, 128, 64, 64, true, true, 4, 1>},
+        DG_PIPE4DW(256, 128, 128, 64, 3),
+        DG_PIPE4DW(128, 128, 64, 64, 4),
     };
     return table[config];
 }
+#undef DG_PIPE4DW
 
 }  // namespace dg

@@ -114,6 +114,16 @@ __device__ __forceinline__ void load_lds16(uint32_t voff, i32x4_rsrc rsrc, unsig
                  : "memory");
 }
 
+// The 4-byte form (fp32 operands whose rows are not 16-byte aligned): lane
+// l's 4 bytes land at lds_addr + 4 * l.
+__device__ __forceinline__ void load_lds4(uint32_t voff, i32x4_rsrc rsrc, unsigned lds_addr)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory");
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 template <int N>
@@ -254,12 +264,18 @@ struct PipeOperandH {
 
 // One fp32 operand of the pipelined kernel (K slab 16).
 //   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
-template <int BMN, bool KCONT, int NW>
+//   LB: bytes per lane per direct load: 16, or 4 for rows that are not
+//   16-byte aligned (any fp32 layout).  The LDS layout is the same; a
+//   4-byte load fills a quarter of the bytes a 16-byte load does, and each
+//   lane fetches the element that belongs at its LDS slot.
+template <int BMN, bool KCONT, int NW, int LB = 16>
 struct PipeOperandS {
+    static_assert(LB == 16 || LB == 4, "16- or 4-byte direct loads");
     static constexpr int BK = 16;
     static constexpr int BYTES = BMN * BK * 4;            // one stage
-    static constexpr int LOADS = BYTES / (NW * 64 * 16);  // 16-byte loads per thread per slab
-    static_assert(LOADS * NW * 64 * 16 == BYTES, "slab must split into 16-byte loads");
+    static constexpr int SPAN = 64 * LB;                   // LDS bytes of one wave-wide load
+    static constexpr int LOADS = BYTES / (NW * SPAN);      // loads per thread per slab
+    static_assert(LOADS * NW * SPAN == BYTES, "slab must split into whole loads");
     static constexpr int ROW_BYTES = KCONT ? BK * 4 : BMN * 4;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
     static_assert(ROWS_PER_LOAD >= 1, "rows of at most 1 KiB");
@@ -268,27 +284,46 @@ struct PipeOperandS {
     uint32_t off[LOADS];         // per-lane byte offsets from base
     int64_t step;                // bytes to advance per slab
 
-    // As the 16-bit operand; offsets stay below 256 * ld * 4 bytes.
+    // The stored element behind LDS byte b of a stage: k row / m-n row r and
+    // the element's place; as the 16-bit operand, offsets stay below
+    // 256 * ld * 4 bytes.
     __device__ __forceinline__ void init(const float *g, int64_t ld, int mn0, int ext, int wave,
                                          int lane)
     {
         base = (const char *)(KCONT ? g + (int64_t)mn0 * ld : g + mn0);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int rbase = (i * NW + wave) * ROWS_PER_LOAD;
-            if constexpr (KCONT) {
-                const int r = rbase + (lane >> 2);
-                const int c = (lane & 3) ^ ((r >> 2) & 3);    // logical 16-byte chunk (4 k)
-                int row = mn0 + r;
-                row = row < ext ? row : ext - 1;
-                off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4) * 4);
+            if constexpr (LB == 16) {
+                const int rbase = (i * NW + wave) * ROWS_PER_LOAD;
+                if constexpr (KCONT) {
+                    const int r = rbase + (lane >> 2);
+                    const int c = (lane & 3) ^ ((r >> 2) & 3);    // logical 16-byte chunk (4 k)
+                    int row = mn0 + r;
+                    row = row < ext ? row : ext - 1;
+                    off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4) * 4);
+                } else {
+                    const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
+                    const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
+                    const int q = (p >> 3) ^ ((r >> 3) & 1);          // logical 128-byte chunk
+                    int col = mn0 + q * 32 + (p & 7) * 4;
+                    col = col < ext ? col : ext - 4;
+                    off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
+                }
             } else {
-                const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
-                const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
-                const int q = (p >> 3) ^ ((r >> 3) & 1);          // logical 128-byte chunk
-                int col = mn0 + q * 32 + (p & 7) * 4;
-                col = col < ext ? col : ext - 4;
-                off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
+                const int b = (i * NW + wave) * SPAN + lane * 4;      // LDS byte in the stage
+                const int r = b / ROW_BYTES, w = b % ROW_BYTES;
+                const int p = w >> 4, e = (w >> 2) & 3;               // 16-byte slot, element
+                if constexpr (KCONT) {
+                    const int c = p ^ ((r >> 2) & 3);
+                    int row = mn0 + r;
+                    row = row < ext ? row : ext - 1;
+                    off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4 + e) * 4);
+                } else {
+                    const int q = (p >> 3) ^ ((r >> 3) & 1);
+                    int col = mn0 + q * 32 + (p & 7) * 4 + e;
+                    col = col < ext ? col : ext - 1;
+                    off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
+                }
             }
         }
         step = (KCONT ? BK : BK * ld) * 4;
@@ -300,29 +335,37 @@ struct PipeOperandS {
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
-            int valid;  // floats of this 16-byte piece that lie before K
-            if constexpr (KCONT) {
-                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> 2);
-                const int c = (lane & 3) ^ ((r >> 2) & 3);
-                valid = krem - c * 4;
-            } else {
-                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
-                valid = r < krem ? 4 : 0;
-            }
             const float *src = (const float *)(base + off[i]);
-            f32x4 v;
-            if (valid >= 4) {
-                v = *(const f32x4 *)src;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x = 0.f;
-                    if (e < valid) x = src[e];
-                    v[e] = x;
+            if constexpr (LB == 16) {
+                lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
+                int valid;  // floats of this 16-byte piece that lie before K
+                if constexpr (KCONT) {
+                    const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> 2);
+                    const int c = (lane & 3) ^ ((r >> 2) & 3);
+                    valid = krem - c * 4;
+                } else {
+                    const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
+                    valid = r < krem ? 4 : 0;
                 }
+                f32x4 v;
+                if (valid >= 4) {
+                    v = *(const f32x4 *)src;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x = 0.f;
+                        if (e < valid) x = src[e];
+                        v[e] = x;
+                    }
+                }
+                *(__attribute__((address_space(3))) f32x4 *)dst = v;
+            } else {
+                const int b = (i * NW + wave) * SPAN + lane * 4;
+                const int r = b / ROW_BYTES, w = b % ROW_BYTES;
+                const int p = w >> 4, e = (w >> 2) & 3;
+                const int k = KCONT ? (p ^ ((r >> 2) & 3)) * 4 + e : r;   // this element's k
+                *(__attribute__((address_space(3))) float *)(lds + b) = k < krem ? *src : 0.f;
             }
-            *(__attribute__((address_space(3))) f32x4 *)dst = v;
         }
         advance();
     }
@@ -338,7 +381,9 @@ struct PipeOperandS {
     // between its MFMAs and calls advance() after the last one).
     __device__ __forceinline__ void issue_one(lds_char_t *lds, int wave, int i)
     {
-        load_lds16(off[i], buffer_rsrc(base), (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024));
+        const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * SPAN);
+        if constexpr (LB == 16) load_lds16(off[i], buffer_rsrc(base), dst);
+        else load_lds4(off[i], buffer_rsrc(base), dst);
     }
 
     // The operand values of MFMA steps 4*c2 .. 4*c2+3 for block rows
@@ -384,10 +429,14 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
 // wave keeps half of its blocks and hands the other half to its partner (the
 // same sub-tile in the other group).  A 256 x 128 tile gets its two waves per
 // SIMD from eight 64 x 64 sub-tiles instead (KSPLIT = 1).
-template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
+// LB: bytes per lane of each direct load, 16, or 4 for fp32 rows that are
+// not 16-byte aligned.
+template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
+          int LB = 16>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_pipe_kernel(GemmParams p)
 {
     constexpr bool HALF = sizeof(T) == 2;          // fp16 or bf16 operands
+    static_assert(LB == 16 || !HALF, "16-bit operands take 16-byte loads");
     typedef T V8 __attribute__((ext_vector_type(8)));
     constexpr int WAVES_N = BN / WN;
     constexpr int NWG = (BM / WM) * WAVES_N;       // waves per K group
@@ -399,8 +448,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     static_assert(KPW >= 1 && KPW * KSPLIT == PIPE_BK / 16, "K split");
     static_assert(KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
     static_assert(HALF || KSPLIT == 1, "fp32 runs without K groups");
-    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW>, PipeOperandS<BM, !TA, NW>>::type OpA;
-    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW>, PipeOperandS<BN, TB, NW>>::type OpB;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW>, PipeOperandS<BM, !TA, NW, LB>>::type OpA;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW>, PipeOperandS<BN, TB, NW, LB>>::type OpB;
     constexpr int BK = OpA::BK;
     constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
     constexpr int SMEM = STAGES * STAGE_BYTES;
@@ -851,13 +900,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT>
+template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
+          int LB = 16>
 hipError_t launch_pipe(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT>,
+    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT, LB>,
                            dim3(nwg, p.batch), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
 }
 
