@@ -209,13 +209,19 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
     const int64_t small = ceil_div(M, 128) * ceil_div(N, 128) * nb;
     const bool pipe = pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x);
     if (dtype == DG_F32) {
-        // 256x128 with two workgroups per CU; the 256x256 eight-wave kernel
-        // measured the same on average over four boxes (each ahead on some:
-        // the spread follows the boxes' clocks, 2.16-2.40 GHz under load)
-        if (pipe) return big >= 384 ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
+        // Rounds of tiles: a CU runs its share of the tiles about ceil(tiles /
+        // 256) tile-times long, whether one or two of them are resident, and a
+        // 256x128 tile takes 1.94 times as long as a 128x128 one (both two
+        // workgroups per CU; measured at 4096 x 4096-4608 x 4096, 3072 x 4096
+        // x 4096, 5120 x 4096 x 2048, 6144^2 x 2048: the 128x128 tile 17-40%
+        // faster wherever the 256x128 tiles end in a partly filled round, 3%
+        // slower at 4096^3, where they fill two rounds exactly).  The 256x256
+        // eight-wave kernel does no better than 256x128 and is not chosen.
+        const int64_t r256 = ceil_div(big, 256), r128 = ceil_div(small, 256);
+        const bool wide = r256 * 194 < r128 * 100;
+        if (pipe) return wide ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
         // rows not 16-byte aligned: the same kernels with 4-byte direct loads
-        if (pipe_dw_ok(A, lda, B, ldb, dtype))
-            return big >= 384 ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
+        if (pipe_dw_ok(A, lda, B, ldb, dtype)) return wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
     // 16-bit operands: the tile is picked by how many CUs its tiles fill

@@ -171,6 +171,21 @@ def test_16bit_large_grids_take_the_tile_that_fills_the_cus_in_one_wave():
             assert "pipe2_ksplit2" not in dg.dg_kernel_name(k)
 
 
+def test_fp32_tile_by_rounds():
+    # 256x128 only where its tiles fill whole rounds of 256 CUs better than
+    # 128x128 tiles do (1.94 tile-times each): the headline 4096^3 and 8192^3
+    for M, N, K, tile in ((4096, 4096, 4096, (256, 128)), (8192, 8192, 8192, (256, 128)),
+                          (4096, 4224, 4096, (128, 128)), (4608, 4096, 4096, (128, 128)),
+                          (3072, 4096, 4096, (128, 128)), (5120, 4096, 2048, (128, 128)),
+                          (2048, 2048, 2048, (128, 128))):
+        assert tile_of(M, N, K, 0) == tile, (M, N, K)
+    # the 4-byte-load kernels follow the same rule (K and N not multiples of 4)
+    k = dg.dg_select_kernel(0, 0, 4095, 4097, 1031, 256, 1031, 256, 4097, 256, 4097, 0)
+    assert dg.dg_kernel_name(k) == "f32_128x128_pipe4_dw_mfma32x32x2"
+    k = dg.dg_select_kernel(0, 0, 4096, 4096, 4095, 256, 4095, 256, 4096, 256, 4096, 0)
+    assert dg.dg_kernel_name(k) == "f32_256x128_pipe3_dw_mfma32x32x2"
+
+
 def test_pipelined_kernels_need_32bit_panel_offsets():
     # a tile panel is addressed with 32-bit byte offsets: 256 rows of the
     # stored matrix must span less than 2^31 bytes, else the register-staged
