@@ -74,6 +74,10 @@ const Family kFamilies[] = {
     {"bf16_256x256_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 256, 4, PIPE, dg::bf16_pipe_launchers, 6},
     {"f32_256x128_pipe3_dw_mfma32x32x2", DG_F32, 256, 128, 8, PIPE_DW, dg::f32_pipe_launchers, 3},
     {"f32_128x128_pipe4_dw_mfma32x32x2", DG_F32, 128, 128, 8, PIPE_DW, dg::f32_pipe_launchers, 4},
+    {"f16_128x128_pipe4_ksplit2_dw_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE_DW, dg::f16_pipe_launchers, 7},
+    {"f16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE_DW, dg::f16_pipe_launchers, 8},
+    {"bf16_128x128_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE_DW, dg::bf16_pipe_launchers, 7},
+    {"bf16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE_DW, dg::bf16_pipe_launchers, 8},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -83,7 +87,8 @@ enum {
     K_BF16_PIPE_256 = 14, K_BF16_PIPE_128_2 = 15, K_F16_PIPE_64 = 16, K_F16_PIPE_128x32 = 17,
     K_F16_PIPE_32x128 = 18, K_BF16_PIPE_64 = 19, K_BF16_PIPE_128x32 = 20, K_BF16_PIPE_32x128 = 21,
     K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23, K_F32_PIPE_256x128_DW = 24,
-    K_F32_PIPE_128_DW = 25
+    K_F32_PIPE_128_DW = 25, K_F16_PIPE_128_DW = 26, K_F16_PIPE_64_DW = 27, K_BF16_PIPE_128_DW = 28,
+    K_BF16_PIPE_64_DW = 29
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -190,12 +195,31 @@ bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int
            (tb || N % v == 0);
 }
 
-// Preconditions of the fp32 pipelined kernels with 4-byte loads: 4-byte
-// aligned A and B (any row stride and extent).
-bool pipe_dw_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype)
+// Preconditions of the pipelined kernels with 4-byte loads: 4-byte aligned
+// rows of A and B; for 16-bit operands (a load takes an element pair) also
+// even row strides and batch strides, and an even m/n-contiguous extent, so
+// that no pair reaches past a row's last element.
+bool pipe_dw_ok(int ta, int tb, int64_t M, int64_t N, const void *A, int64_t lda, const void *B,
+                int64_t ldb, int dtype, const Ext &x)
 {
-    return dtype == DG_F32 && ((uintptr_t)A & 3) == 0 && ((uintptr_t)B & 3) == 0 &&
-           offsets_fit(lda, ldb, dtype);
+    if (((uintptr_t)A & 3) != 0 || ((uintptr_t)B & 3) != 0 || !offsets_fit(lda, ldb, dtype)) return false;
+    if (dtype == DG_F32) return true;
+    return lda % 2 == 0 && ldb % 2 == 0 && (x.batch <= 1 || (x.sA % 2 == 0 && x.sB % 2 == 0)) &&
+           (!ta || M % 2 == 0) && (tb || N % 2 == 0);
+}
+
+// The 4-byte-load counterpart of a 16-byte-load 16-bit kernel: the 64x64
+// tile for the narrow ones, else the 128x128 tile (the larger tiles with
+// 4-byte loads would spill their per-lane offsets).
+int dw_kernel(int k, bool bf)
+{
+    switch (k) {
+    case K_F16_PIPE_64: case K_F16_PIPE_128x32: case K_F16_PIPE_32x128:
+    case K_BF16_PIPE_64: case K_BF16_PIPE_128x32: case K_BF16_PIPE_32x128:
+        return bf ? K_BF16_PIPE_64_DW : K_F16_PIPE_64_DW;
+    default:
+        return bf ? K_BF16_PIPE_128_DW : K_F16_PIPE_128_DW;
+    }
 }
 
 // Kernel choice by dtype, preconditions and output tile count.  Larger tiles
@@ -221,12 +245,12 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         const bool wide = r256 * 194 < r128 * 100;
         if (pipe) return wide ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
         // rows not 16-byte aligned: the same kernels with 4-byte direct loads
-        if (pipe_dw_ok(A, lda, B, ldb, dtype)) return wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
+        if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
     // 16-bit operands: the tile is picked by how many CUs its tiles fill
     const bool bf = dtype == DG_BF16_F32ACC;
-    if (pipe) {
+    auto pick = [&]() -> int {
         // narrow outputs take tiles that match them instead of padding a
         // 128-wide tile: N or M of 32 (low-rank products), 64 (attention's
         // per-head products with d_head = 64)
@@ -266,7 +290,10 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64) * nb;
         if (small <= 128 && t64 >= 256 && K <= 8192) return bf ? K_BF16_PIPE_64 : K_F16_PIPE_64;
         return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
-    }
+    };
+    if (pipe) return pick();
+    // rows 4-byte but not 16-byte aligned: the same tiles with 4-byte loads
+    if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return dw_kernel(pick(), bf);
     if (bf) return K_BF16_SIMPLE;
     return big >= 512 ? K_F16_256 : K_F16_128;
 }
@@ -279,7 +306,7 @@ bool supports(int kernel, int ta, int tb, int64_t M, int64_t N, int64_t K, const
     if (f.dtype != dtype) return false;
     if (f.kind == SIMPLE) return ceil_div(M, 64) <= 65535;
     if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x)) return false;
-    if (f.kind == PIPE_DW && !pipe_dw_ok(A, lda, B, ldb, dtype)) return false;
+    if (f.kind == PIPE_DW && !pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return false;
     return ceil_div(M, f.bm) * ceil_div(N, f.bn) <= 0x7fffffff;
 }
 

@@ -36,12 +36,18 @@ const launch_fn *f16_launchers(int config)
 //   4: 128x32 tile, 4 stages, four 32x32 waves (N = 32: low-rank products)
 //   5: 32x128 tile, 4 stages, four 32x32 waves (M = 32)
 //   6: 256x256 tile, 2 stages, eight 128x64 waves (large squares)
+//   7, 8: configs 0 and 3 with 4-byte direct loads (rows 4-byte but not
+//      16-byte aligned; the larger tiles would spill the four times as many
+//      per-lane offsets)
 #define DG_PIPE4(T, BM, BN, WM, WN, ST, KS)                                                   \
     {launch_pipe<T, BM, BN, WM, WN, false, false, ST, KS>, launch_pipe<T, BM, BN, WM, WN, false, true, ST, KS>, \
      launch_pipe<T, BM, BN, WM, WN, true, false, ST, KS>, launch_pipe<T, BM, BN, WM, WN, true, true, ST, KS>}
+#define DG_PIPE4DW(T, BM, BN, WM, WN, ST, KS)                                                 \
+    {launch_pipe<T, BM, BN, WM, WN, false, false, ST, KS, 4>, launch_pipe<T, BM, BN, WM, WN, false, true, ST, KS, 4>, \
+     launch_pipe<T, BM, BN, WM, WN, true, false, ST, KS, 4>, launch_pipe<T, BM, BN, WM, WN, true, true, ST, KS, 4>}
 const launch_fn *f16_pipe_launchers(int config)
 {
-    static const launch_fn table[7][4] = {
+    static const launch_fn table[9][4] = {
         DG_PIPE4(_Float16, 128, 128, 64, 64, 4, 2),
         DG_PIPE4(_Float16, 256, 128, 64, 64, 3, 1),
         DG_PIPE4(_Float16, 128, 128, 64, 64, 2, 2),
@@ -49,9 +55,12 @@ const launch_fn *f16_pipe_launchers(int config)
         DG_PIPE4(_Float16, 128, 32, 32, 32, 4, 1),
         DG_PIPE4(_Float16, 32, 128, 32, 32, 4, 1),
         DG_PIPE4(_Float16, 256, 256, 128, 64, 2, 1),
+        DG_PIPE4DW(_Float16, 128, 128, 64, 64, 4, 2),
+        DG_PIPE4DW(_Float16, 64, 64, 64, 32, 4, 2),
     };
     return table[config];
 }
 #undef DG_PIPE4
+#undef DG_PIPE4DW
 
 }  // namespace dg

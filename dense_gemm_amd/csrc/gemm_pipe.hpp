@@ -114,8 +114,8 @@ __device__ __forceinline__ void load_lds16(uint32_t voff, i32x4_rsrc rsrc, unsig
                  : "memory");
 }
 
-// The 4-byte form (fp32 operands whose rows are not 16-byte aligned): lane
-// l's 4 bytes land at lds_addr + 4 * l.
+// The 4-byte form (operands whose rows are not 16-byte aligned): lane l's 4
+// bytes land at lds_addr + 4 * l.
 __device__ __forceinline__ void load_lds4(uint32_t voff, i32x4_rsrc rsrc, unsigned lds_addr)
 {
     asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
@@ -135,14 +135,21 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // One 16-bit operand (fp16 or bf16) of the pipelined kernel (K slab 64).
 //   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
-template <typename E, int BMN, bool KCONT, int NW>
+//   LB: bytes per lane per direct load: 16, or 4 (two elements) for rows
+//   that are 4-byte but not 16-byte aligned.  The LDS layout is the same;
+//   each lane fetches the element pair that belongs at its LDS slot.
+template <typename E, int BMN, bool KCONT, int NW, int LB = 16>
 struct PipeOperandH {
+    static_assert(LB == 16 || LB == 4, "16- or 4-byte direct loads");
     typedef E V8 __attribute__((ext_vector_type(8)));
+    typedef E V2 __attribute__((ext_vector_type(2)));
     typedef __attribute__((address_space(3))) V8 lds_v8_t;
+    typedef __attribute__((address_space(3))) V2 lds_v2_t;
     static constexpr int BK = PIPE_BK;
     static constexpr int BYTES = BMN * PIPE_BK * 2;      // one stage
-    static constexpr int LOADS = BYTES / (NW * 64 * 16);  // 16-byte loads per thread per slab
-    static_assert(LOADS * NW * 64 * 16 == BYTES, "slab must split into 16-byte loads");
+    static constexpr int SPAN = 64 * LB;                  // LDS bytes of one wave-wide load
+    static constexpr int LOADS = BYTES / (NW * SPAN);     // loads per thread per slab
+    static_assert(LOADS * NW * SPAN == BYTES, "slab must split into whole loads");
     static constexpr int ROW_BYTES = KCONT ? PIPE_BK * 2 : BMN * 2;
     static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;  // rows one wave-wide load fills
     static constexpr int QUADS = ROW_BYTES / 64;             // 64-byte quads per row (m/n-contiguous)
@@ -167,20 +174,37 @@ struct PipeOperandH {
         base = (const char *)(KCONT ? g + (int64_t)mn0 * ld : g + mn0);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int rbase = (i * NW + wave) * ROWS_PER_LOAD;  // first LDS row of this load
-            if constexpr (KCONT) {
-                const int r = rbase + (lane >> 3);
-                const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical 16-byte chunk (8 k)
-                int row = mn0 + r;
-                row = row < ext ? row : ext - 1;
-                off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 8) * 2);
+            if constexpr (LB == 16) {
+                const int rbase = (i * NW + wave) * ROWS_PER_LOAD;  // first LDS row of this load
+                if constexpr (KCONT) {
+                    const int r = rbase + (lane >> 3);
+                    const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical 16-byte chunk (8 k)
+                    int row = mn0 + r;
+                    row = row < ext ? row : ext - 1;
+                    off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 8) * 2);
+                } else {
+                    const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
+                    const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
+                    const int q = (p >> 2) ^ swz(r);                  // logical 64-byte quad
+                    int col = mn0 + q * 32 + (p & 3) * 8;
+                    col = col < ext ? col : ext - 8;
+                    off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 2);
+                }
             } else {
-                const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
-                const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
-                const int q = (p >> 2) ^ swz(r);                  // logical 64-byte quad
-                int col = mn0 + q * 32 + (p & 3) * 8;
-                col = col < ext ? col : ext - 8;
-                off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 2);
+                const int b = (i * NW + wave) * SPAN + lane * 4;      // LDS byte in the stage
+                const int r = b / ROW_BYTES, w = b % ROW_BYTES;
+                const int p = w >> 4, e = (w >> 2) & 3;               // 16-byte slot, element pair
+                if constexpr (KCONT) {
+                    const int c = p ^ ((r >> 1) & 7);
+                    int row = mn0 + r;
+                    row = row < ext ? row : ext - 1;
+                    off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 8 + 2 * e) * 2);
+                } else {
+                    const int q = (p >> 2) ^ swz(r);
+                    int col = mn0 + q * 32 + (p & 3) * 8 + 2 * e;
+                    col = col < ext ? col : ext - 2;                  // ext is even here
+                    off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 2);
+                }
             }
         }
         step = (KCONT ? PIPE_BK : PIPE_BK * ld) * 2;
@@ -195,29 +219,41 @@ struct PipeOperandH {
     {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
-            int valid;  // halfs of this 16-byte piece that lie before K
-            if constexpr (KCONT) {
-                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> 3);
-                const int c = (lane & 7) ^ ((r >> 1) & 7);
-                valid = krem - c * 8;
-            } else {
-                const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
-                valid = r < krem ? 8 : 0;
-            }
             const E *src = (const E *)(base + off[i]);
-            V8 v;
-            if (valid >= 8) {
-                v = *(const V8 *)src;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    E x = (E)0.f;
-                    if (e < valid) x = src[e];
-                    v[e] = x;
+            if constexpr (LB == 16) {
+                lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
+                int valid;  // halfs of this 16-byte piece that lie before K
+                if constexpr (KCONT) {
+                    const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> 3);
+                    const int c = (lane & 7) ^ ((r >> 1) & 7);
+                    valid = krem - c * 8;
+                } else {
+                    const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
+                    valid = r < krem ? 8 : 0;
                 }
+                V8 v;
+                if (valid >= 8) {
+                    v = *(const V8 *)src;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        E x = (E)0.f;
+                        if (e < valid) x = src[e];
+                        v[e] = x;
+                    }
+                }
+                *(lds_v8_t *)dst = v;
+            } else {
+                const int b = (i * NW + wave) * SPAN + lane * 4;
+                const int r = b / ROW_BYTES, w = b % ROW_BYTES;
+                const int p = w >> 4, e = (w >> 2) & 3;
+                // halfs of this pair that lie before K
+                const int valid = KCONT ? krem - ((p ^ ((r >> 1) & 7)) * 8 + 2 * e) : (r < krem ? 2 : 0);
+                V2 v;
+                v[0] = valid >= 1 ? src[0] : (E)0.f;
+                v[1] = valid >= 2 ? src[1] : (E)0.f;
+                *(lds_v2_t *)(lds + b) = v;
             }
-            *(lds_v8_t *)dst = v;
         }
         advance();
     }
@@ -234,7 +270,9 @@ struct PipeOperandH {
     // between its MFMAs and calls advance() after the last one).
     __device__ __forceinline__ void issue_one(lds_char_t *lds, int wave, int i)
     {
-        load_lds16(off[i], buffer_rsrc(base), (unsigned)(uintptr_t)(lds + (i * NW + wave) * 1024));
+        const unsigned dst = (unsigned)(uintptr_t)(lds + (i * NW + wave) * SPAN);
+        if constexpr (LB == 16) load_lds16(off[i], buffer_rsrc(base), dst);
+        else load_lds4(off[i], buffer_rsrc(base), dst);
     }
 
     // MFMA operand of block rows [b0, b0+32) for k-step kk (16 k) of a stage.
@@ -429,14 +467,13 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
 // wave keeps half of its blocks and hands the other half to its partner (the
 // same sub-tile in the other group).  A 256 x 128 tile gets its two waves per
 // SIMD from eight 64 x 64 sub-tiles instead (KSPLIT = 1).
-// LB: bytes per lane of each direct load, 16, or 4 for fp32 rows that are
-// not 16-byte aligned.
+// LB: bytes per lane of each direct load, 16, or 4 for rows that are not
+// 16-byte aligned.
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
           int LB = 16>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_pipe_kernel(GemmParams p)
 {
     constexpr bool HALF = sizeof(T) == 2;          // fp16 or bf16 operands
-    static_assert(LB == 16 || !HALF, "16-bit operands take 16-byte loads");
     typedef T V8 __attribute__((ext_vector_type(8)));
     constexpr int WAVES_N = BN / WN;
     constexpr int NWG = (BM / WM) * WAVES_N;       // waves per K group
@@ -448,8 +485,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     static_assert(KPW >= 1 && KPW * KSPLIT == PIPE_BK / 16, "K split");
     static_assert(KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
     static_assert(HALF || KSPLIT == 1, "fp32 runs without K groups");
-    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW>, PipeOperandS<BM, !TA, NW, LB>>::type OpA;
-    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW>, PipeOperandS<BN, TB, NW, LB>>::type OpB;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW, LB>, PipeOperandS<BM, !TA, NW, LB>>::type OpA;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW, LB>, PipeOperandS<BN, TB, NW, LB>>::type OpB;
     constexpr int BK = OpA::BK;
     constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
     constexpr int SMEM = STAGES * STAGE_BYTES;

@@ -345,3 +345,41 @@ def test_sgemm_ragged_full_form(dg, shape, ta, tb):
     p = Problem(a, b, c0, ta, tb, 1.5, -0.5, "f32", (8, 8, 8))
     print(f"ragged {shape} ta={ta} tb={tb}", flush=True)
     check_sampled(p, n=2000, seed=5)
+
+
+# ---------------------------------------------------------------------------
+# 4-byte direct loads: rows 4-byte but not 16-byte aligned (ld padded so)
+# ---------------------------------------------------------------------------
+def _pad_4byte_rows(base, dtype):
+    """Padding d >= 1 that makes base + d a row stride of 4-byte but not
+    16-byte multiples (fp32: not a multiple of 4 elements; 16-bit: even, not
+    a multiple of 8)."""
+    for d in range(1, 9):
+        ld = base + d
+        if dtype == "f32" and ld % 4 != 0:
+            return d
+        if dtype != "f32" and ld % 2 == 0 and ld % 8 != 0:
+            return d
+    raise AssertionError(base)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("ta,tb", TRANS)
+@pytest.mark.parametrize("shape", [(300, 258, 131), (130, 66, 70), (520, 514, 1030)])
+def test_four_byte_direct_loads(dg, dtype, ta, tb, shape):
+    """The library's own choice on row strides that rule out 16-byte loads:
+    a pipelined kernel with 4-byte loads (`_dw`), every output against the
+    oracle, alpha/beta applied, C's padding untouched.  Odd K puts a pair of
+    16-bit elements across the end of K in the last slab."""
+    M, N, K = shape
+    dist = "uniform" if dtype == "f32" else "normal_sqrtk"
+    a, b, c0 = synth.problem(M, N, K, dtype, dist, 540 + M + K, with_c0=True)
+    pa = _pad_4byte_rows(M if ta else K, dtype)
+    pb = _pad_4byte_rows(K if tb else N, dtype)
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype, pad=(pa, pb, 3))
+    k = dg.dg_select_kernel(int(ta), int(tb), M, N, K, 256, p.lda, 256, p.ldb, 256, p.ldc,
+                            {"f32": 0, "f16": 1, "bf16": 2}[dtype])
+    assert "_dw_" in dg.dg_kernel_name(k), dg.dg_kernel_name(k)
+    print(f"4-byte loads {dtype} {shape} ta={ta} tb={tb} lda={p.lda} ldb={p.ldb} "
+          f"kernel={dg.dg_kernel_name(k)}", flush=True)
+    check_full(p, out=p.run_gpu())
