@@ -17,6 +17,7 @@ const launch_fn *f16_launchers(int config);
 const launch_fn *f16_pipe_launchers(int config);
 const launch_fn *f32_pipe_launchers(int config);
 const launch_fn *bf16_pipe_launchers(int config);
+const launch_fn *bf16_launchers(int config);
 }  // namespace dg
 
 namespace {
@@ -78,6 +79,8 @@ const Family kFamilies[] = {
     {"f16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE_DW, dg::f16_pipe_launchers, 8},
     {"bf16_128x128_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE_DW, dg::bf16_pipe_launchers, 7},
     {"bf16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE_DW, dg::bf16_pipe_launchers, 8},
+    {"bf16_128x128_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, MFMA, dg::bf16_launchers, 0},
+    {"bf16_256x128_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, MFMA, dg::bf16_launchers, 1},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -88,7 +91,7 @@ enum {
     K_F16_PIPE_32x128 = 18, K_BF16_PIPE_64 = 19, K_BF16_PIPE_128x32 = 20, K_BF16_PIPE_32x128 = 21,
     K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23, K_F32_PIPE_256x128_DW = 24,
     K_F32_PIPE_128_DW = 25, K_F16_PIPE_128_DW = 26, K_F16_PIPE_64_DW = 27, K_BF16_PIPE_128_DW = 28,
-    K_BF16_PIPE_64_DW = 29
+    K_BF16_PIPE_64_DW = 29, K_BF16_128 = 30, K_BF16_256 = 31
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -294,7 +297,7 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
     if (pipe) return pick();
     // rows 4-byte but not 16-byte aligned: the same tiles with 4-byte loads
     if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return dw_kernel(pick(), bf);
-    if (bf) return K_BF16_SIMPLE;
+    if (bf) return big >= 512 ? K_BF16_256 : K_BF16_128;
     return big >= 512 ? K_F16_256 : K_F16_128;
 }
 

@@ -1,9 +1,34 @@
 // bf16-operand, fp32-accumulate kernel instantiations
 // (v_mfma_f32_32x32x16_bf16): the pipelined kernels of gemm_pipe.hpp with
 // bf16 elements, in the fp16 kernels' configurations.
+#include "gemm_mfma.hpp"
 #include "gemm_pipe.hpp"
 
 namespace dg {
+
+#define DG_VARIANTS(T, BM, BN, BK, WM, WN, MINW)                                         \
+    {                                                                                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, false, true, MINW>,                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, true, true, MINW>,                    \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, false, true, MINW>,                    \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, true, true, MINW>,                     \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, false, false, MINW>,                  \
+        launch_mfma<T, BM, BN, BK, WM, WN, false, true, false, MINW>,                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, false, false, MINW>,                   \
+        launch_mfma<T, BM, BN, BK, WM, WN, true, true, false, MINW>,                    \
+    }
+
+// register-staged kernels (operands no pipelined kernel takes: odd row
+// strides or m/n extents): [config][vec ? 0 : 4 + transA * 2 + transB]
+const launch_fn *bf16_launchers(int config)
+{
+    static const launch_fn table[2][8] = {
+        DG_VARIANTS(__bf16, 128, 128, 64, 64, 64, 1),
+        DG_VARIANTS(__bf16, 256, 128, 64, 128, 64, 1),
+    };
+    return table[config];
+}
+#undef DG_VARIANTS
 
 // pipelined direct-to-LDS kernels: [config][transA * 2 + transB]
 //   0: 128x128 tile, 4 stages, two K groups of 4 waves (one workgroup per CU)

@@ -55,6 +55,10 @@ template <> struct ElemTraits<_Float16> {
     static constexpr int V = 8;
     typedef f16x8 vec;
 };
+template <> struct ElemTraits<__bf16> {
+    static constexpr int V = 8;
+    typedef bf16x8 vec;
+};
 
 // Load V consecutive elements p[0 .. V-1]; elements at or beyond `valid` are
 // zero and are not read.
@@ -69,7 +73,7 @@ __device__ __forceinline__ typename ElemTraits<T>::vec load_vec(const T *p, int 
     } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            T x = (T)0;
+            T x = (T)0.f;
             if (e < valid) x = p[e];
             v[e] = x;
         }
@@ -156,7 +160,7 @@ struct Operand {
             // register transpose: column j of the KV x V block becomes a run
             // of KV k-values in LDS row (c + j)
             const int kg = tid / LPK, c = (tid % LPK) * V;
-            typedef _Float16 run_t __attribute__((ext_vector_type(KV)));
+            typedef T run_t __attribute__((ext_vector_type(KV)));
 #pragma unroll
             for (int j = 0; j < V; ++j) {
                 run_t t;
@@ -269,18 +273,19 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
             // fp16: 32x32x16 MFMA, BK/16 steps, 8 k per lane per step
 #pragma unroll
             for (int c = 0; c < BK / 16; ++c) {
-                f16x8 a[TM], b[TN];
+                typedef typename ElemTraits<T>::vec v8;
+                v8 a[TM], b[TN];
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    a[i] = *(const f16x8 *)(sA + (wm0 + 32 * i + lrow) * OpA::LD + khalf + 8 * c);
+                    a[i] = *(const v8 *)(sA + (wm0 + 32 * i + lrow) * OpA::LD + khalf + 8 * c);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    b[j] = *(const f16x8 *)(sB + (wn0 + 32 * j + lrow) * OpB::LD + khalf + 8 * c);
+                    b[j] = *(const v8 *)(sB + (wn0 + 32 * j + lrow) * OpB::LD + khalf + 8 * c);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = mfma_32x32x16(a[i], b[j], acc[i][j]);
             }
         }
         if (more) {

@@ -448,15 +448,6 @@ struct PipeOperandS {
     }
 };
 
-// The 32x32x16 matrix-core step for either 16-bit operand type (fp32 accumulators).
-__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // Waves: (BM/WM) x (BN/WN) sub-tiles per K group, KSPLIT groups.  Group g
 // runs the 16-k steps [g*4/KSPLIT, (g+1)*4/KSPLIT) of every slab, so with a

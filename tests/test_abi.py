@@ -115,10 +115,8 @@ def test_selection_picks_matrix_core_kernels_of_the_right_type():
             k = dg.dg_select_kernel(0, 0, M, N, K, NULL, K, NULL, N, NULL, N, dtype)
             name = dg.dg_kernel_name(k)
             assert name.startswith(prefix), (M, N, K, name)
-            # bf16 has only the pipelined matrix-core kernels; rows that are not
-            # whole 16-byte pieces fall back to the generic kernel
-            aligned = K % 8 == 0 and N % 8 == 0
-            assert ("mfma" in name) == (dtype != 2 or aligned), (M, N, K, name)
+            # every type has matrix-core kernels for any alignment
+            assert "mfma" in name, (M, N, K, name)
     # the headline shapes get the large tiles
     k = dg.dg_select_kernel(0, 0, 4096, 4096, 4096, NULL, 4096, NULL, 4096, NULL, 4096, 0)
     assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 128)
