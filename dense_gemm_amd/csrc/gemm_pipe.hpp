@@ -50,23 +50,28 @@
 // The swizzle is applied by choosing which global address each lane fetches,
 // since a direct load writes its lanes contiguously.
 //
-// Pipeline per K slab kt (one barrier per slab), fp16:
+// Pipeline per K slab kt (one barrier per slab), 16-bit tiles up to 256 x 128:
 //   wait for this thread's loads of slab kt+1; barrier (slab kt+1 visible to
 //   all, and every wave holds its fragments of slab kt in registers); issue
-//   the loads of slab kt+STAGES into the stage slab kt used; read the
-//   fragments of slab kt+1 into the second register set while the MFMAs of
-//   slab kt run.  fp32 (whose larger wave tiles leave no registers for a
-//   second fragment set): wait for slab kt; barrier; issue slab kt+STAGES-1
-//   into the stage of slab kt-1; fragment reads and MFMAs of slab kt.
-//   (Moving the barrier into the middle of a slab, to overlap the next slab's
-//   first LDS reads with MFMAs, measured slower: it drains the MFMA queue
-//   mid-slab.)
+//   the loads of a later slab into a stage whose fragments every wave has
+//   read; read the fragments of slab kt+1 into the second register set while
+//   the MFMAs of slab kt run.  16-bit 256 x 256 tiles (whose accumulators
+//   leave registers for one k step's fragments, not a slab's): the barrier
+//   sits before each slab's last k step, which overlaps the next slab's first
+//   fragment reads (see the loop).  fp32 (whose larger wave tiles leave no
+//   registers for a second fragment set): wait for slab kt; barrier; issue
+//   slab kt+STAGES-1 into the stage of slab kt-1; fragment reads and MFMAs
+//   of slab kt.  (For fp32, moving the barrier into the middle of a slab
+//   measured slower: it drains the MFMA queue mid-slab.)
 //
-// Host-side preconditions (checked by the dispatcher): A and B 16-byte
-// aligned with lda, ldb multiples of 16 bytes; the m/n-contiguous operand's
-// extent (M if A is transposed, N if B is not) a multiple of 16 bytes.  A
-// last slab shorter than BK is loaded through registers with zero fill.  Rows or
-// columns past M or N are fetched from a clamped, valid address; they only
+// Host-side preconditions (checked by the dispatcher): 16-byte loads (LB =
+// 16) need A and B 16-byte aligned with lda, ldb multiples of 16 bytes and
+// the m/n-contiguous operand's extent (M if A is transposed, N if B is not) a
+// multiple of 16 bytes; 4-byte loads (LB = 4) need 4-byte alignment, and for
+// 16-bit operands even strides and an even m/n-contiguous extent.  256 rows
+// of each stored operand must span less than 2^31 bytes (32-bit offsets).  A
+// last slab shorter than BK is loaded through registers with zero fill.  Rows
+// or columns past M or N are fetched from a clamped, valid address; they only
 // feed outputs that the guarded epilogue never stores.
 #pragma once
 
