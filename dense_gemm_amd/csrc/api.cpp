@@ -248,7 +248,8 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         const bool wide = r256 * 194 < r128 * 100;
         if (pipe) return wide ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
         // rows not 16-byte aligned: the same kernels with 4-byte direct loads
-        if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
+        if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x))
+            return wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
     // 16-bit operands: the tile is picked by how many CUs its tiles fill
