@@ -1,0 +1,55 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract, the amd-smi
+clock parser, and that the committed counter summary belongs to the kernel
+sources in the tree (else bench.py would report its traffic as null)."""
+import json
+import os
+import subprocess
+import sys
+import types
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _fake_run(stdout):
+    return lambda *a, **k: types.SimpleNamespace(stdout=stdout, returncode=0)
+
+
+def test_smi_clock_parser(monkeypatch):
+    clk = lambda v: {"value": v, "unit": "MHz"}
+    gfx = {f"gfx_{i}": {"clk": clk(2100 + i), "min_clk": clk(500), "max_clk": clk(2400),
+                        "clk_locked": "DISABLED", "deep_sleep": "ENABLED"} for i in range(8)}
+    gfx["mem_0"] = {"clk": clk(2000), "min_clk": clk(2000), "max_clk": clk(2000),
+                    "clk_locked": "N/A", "deep_sleep": "DISABLED"}
+    gfx["fclk_0"] = {"clk": "N/A", "min_clk": "N/A", "max_clk": "N/A"}
+    monkeypatch.setattr(subprocess, "run", _fake_run(json.dumps({"gpu_data": [{"gpu": 0, "clock": gfx}]})))
+    got = bench.smi_clocks()
+    assert got == {"gfx_mhz_median": 2104, "gfx_min_mhz": 500, "gfx_max_mhz": 2400,
+                   "gfx_locked": "DISABLED", "mem_mhz": 2000}
+
+
+def test_smi_clock_parser_failures(monkeypatch):
+    monkeypatch.setattr(subprocess, "run", _fake_run("not json"))
+    assert bench.smi_clocks() is None
+
+    def missing(*a, **k):
+        raise FileNotFoundError("amd-smi")
+    monkeypatch.setattr(subprocess, "run", missing)
+    assert bench.smi_clocks() is None
+
+
+def test_committed_counters_match_the_kernel_sources():
+    import dense_gemm_amd as dg
+    k = dg.dg_select_kernel(0, 0, 4096, 4096, 4096, 256, 4096, 256, 4096, 256, 4096, dg.DG_F32)
+    traffic = bench.measured_traffic(k, 0, 0, 4096, 4096)
+    assert traffic is not None, "profiles/hbm_traffic.txt was taken from other kernel sources"
+    # at least the algorithmic bytes (A and B read once, C written once)
+    assert traffic >= 3 * 4096 * 4096 * 4
