@@ -565,9 +565,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
         // and its fragment reads, and the workgroup meets at a barrier: slab
         // kt+1 is visible, and every wave is done with slab kt's stage.  The
         // last k step then runs while slab kt+1's first fragments are read
-        // and slab kt+2 is loaded into slab kt's stage, one load before each
-        // MFMA.  So no fragment read waits at a barrier, and each load has
-        // KPW-1 k steps of the next slab to land.  The reads after the last
+        // and slab kt+2's A is loaded into slab kt's stage; its B follows
+        // during k step 0 of slab kt+1 (a load every second MFMA in both:
+        // 1.6-2% faster at 4096^3, 5-7% at 3072^3 than all of them in the
+        // last k step).  So no fragment read waits at a barrier, and each
+        // load has at least KPW-2 k steps to land.  The reads after the last
         // slab fetch a stale stage that is never used (no branch between
         // them and the MFMAs).
         V8 fa[2][TM], fb[2][TN];
@@ -580,6 +582,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
 #pragma unroll
         for (int j = 0; j < TN; ++j) fb[0][j] = gb.frag(smem + OpA::BYTES, wn0 + 32 * j, kk0, lane);
         if (nk > 1) issue_slab(1, smem + STAGE_BYTES);
+        bool pend = false;                      // B's loads of a slab deferred to k step 0
+        lds_char_t *pdst = smem;
         for (int kt = 0; kt < nk; ++kt) {
             const lds_char_t *sA = smem + (kt % STAGES) * STAGE_BYTES;
             const lds_char_t *sB = sA + OpA::BYTES;
@@ -591,11 +595,17 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
 #pragma unroll
                     for (int j = 0; j < TN; ++j) {
                         const int f = i * TN + j;        // fragment of the next k step
+                        if (s == 0) {
+#pragma unroll
+                            for (int l = 0; l < OpB::LOADS; ++l)
+                                if (l * NL / OpB::LOADS == f && pend) gb.issue_one(pdst + OpA::BYTES, wave, l);
+                        }
                         if (f < TM) fa[nxt][f] = ga.frag(sA, wm0 + 32 * f, kk0 + s + 1, lane);
                         else if (f < TM + TN) fb[nxt][f - TM] = gb.frag(sB, wn0 + 32 * (f - TM), kk0 + s + 1, lane);
                         acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
+                if (s == 0 && pend) gb.advance();
             }
             wait_vmcnt<0>();
             __syncthreads();
@@ -612,21 +622,16 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                 for (int j = 0; j < TN; ++j) {
                     const int m = i * TN + j;
 #pragma unroll
-                    for (int l = 0; l < LOADS; ++l) {
-                        if (l * NL / LOADS == m && spread) {
-                            if (l < OpA::LOADS) ga.issue_one(dst, wave, l);
-                            else gb.issue_one(dst + OpA::BYTES, wave, l - OpA::LOADS);
-                        }
-                    }
+                    for (int l = 0; l < OpA::LOADS; ++l)
+                        if (l * NL / OpA::LOADS == m && spread) ga.issue_one(dst, wave, l);
                     if (m < TM) fa[nxt][m] = ga.frag(rA, wm0 + 32 * m, kk0, lane);
                     else if (m < TM + TN) fb[nxt][m - TM] = gb.frag(rB, wn0 + 32 * (m - TM), kk0, lane);
                     acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            if (spread) {
-                ga.advance();
-                gb.advance();
-            }
+            if (spread) ga.advance();
+            pend = spread;
+            pdst = dst;
         }
     } else if constexpr (HALF) {
         // Two fragment sets, the loop unrolled by two so that each set stays
