@@ -845,7 +845,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     // columns 16*(l%2) .. +15, forms alpha*acc + beta*C + bias and the
     // activation in fp32, and writes them with 16-byte stores (one rounding to
     // the output type per element), or element by element at the matrix edge
-    // or when C rows are not 16-byte aligned.
+    // or when C rows are not 16-byte aligned.  The 16-byte stores of a 16-bit
+    // C carry the non-temporal hint (C is not read again by the kernel); fp32
+    // C and the 256x128 tile keep plain stores, which measured faster there.
+    constexpr bool NT_STORE = HALF && !(BM == 256 && BN == 128);
     T *C = (T *)p.C;
     lds_char_t *stg = smem + wave * 32 * EPI_LD * 4;
     typedef __attribute__((address_space(3))) float lds_float_t;
@@ -919,8 +922,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                     o0[e] = (T)v[e];
                     o1[e] = (T)v[8 + e];
                 }
-                *(V8 *)c = o0;
-                *(V8 *)(c + 8) = o1;
+                if constexpr (NT_STORE) {
+                    __builtin_nontemporal_store(o0, (V8 *)c);
+                    __builtin_nontemporal_store(o1, (V8 *)(c + 8));
+                } else {
+                    *(V8 *)c = o0;
+                    *(V8 *)(c + 8) = o1;
+                }
             } else {
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4)
