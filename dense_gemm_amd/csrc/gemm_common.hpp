@@ -108,125 +108,97 @@ __device__ __forceinline__ float epilogue_value(const GemmParams &p, float acc, 
     return activate(p.act, v);
 }
 
-// The same for 16 consecutive columns col .. col+15 (all < N): the bias is
-// read with 16-byte loads when its address allows.
-template <typename T>
-__device__ __forceinline__ void epilogue_row16(const GemmParams &p, float (&v)[16], const float (&cin)[16],
-                                               int col)
+// The same for W consecutive columns col .. col+W-1 (all < N): the bias is
+// read with vector loads (16 bytes, or the W elements when they are fewer)
+// when its address allows.
+template <typename T, int W>
+__device__ __forceinline__ void epilogue_row(const GemmParams &p, float (&v)[W], const float (&cin)[W], int col)
 {
-    float b[16];
+    constexpr int PER = (int)(16 / sizeof(T)) < W ? (int)(16 / sizeof(T)) : W;  // elements per bias load
+    float b[W];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) b[e] = 0.f;
+    for (int e = 0; e < W; ++e) b[e] = 0.f;
     if (p.bias) {
         const T *bp = (const T *)p.bias + col;
-        if (((uintptr_t)bp & 15) == 0) {
-            constexpr int PER = 16 / sizeof(T);
+        if (((uintptr_t)bp & (PER * sizeof(T) - 1)) == 0) {
             typedef T VT __attribute__((ext_vector_type(PER)));
 #pragma unroll
-            for (int c = 0; c < 16 / PER; ++c) {
+            for (int c = 0; c < W / PER; ++c) {
                 const VT x = *(const VT *)(bp + c * PER);
 #pragma unroll
                 for (int e = 0; e < PER; ++e) b[c * PER + e] = (float)x[e];
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) b[e] = (float)bp[e];
+            for (int e = 0; e < W; ++e) b[e] = (float)bp[e];
         }
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < W; ++e) {
         float x = p.alpha * v[e];
         if (p.beta != 0.f) x = __builtin_fmaf(p.beta, cin[e], x);
         v[e] = activate(p.act, x + b[e]);
     }
 }
 
-// Split-K reduction of 16 consecutive columns c0 .. c0+15 of row `row` (only
+template <typename T>
+__device__ __forceinline__ void epilogue_row16(const GemmParams &p, float (&v)[16], const float (&cin)[16],
+                                               int col)
+{
+    epilogue_row<T, 16>(p, v, cin, col);
+}
+
+// Split-K reduction of 4 consecutive columns c0 .. c0+3 of row `row` (only
 // those below N): the splits' fp32 partials (ws[s] is M x N, row stride N)
 // summed in increasing s starting from zero, then alpha, beta, bias and the
 // activation in fp32 and one rounding to T.  beta == 0 does not read C.
 // Partials are read with 16-byte loads when N is a multiple of 4 (the
-// workspace is 16-byte aligned), four splits' loads in flight at once; C is
-// written with 16-byte stores when its rows allow.
+// workspace is 16-byte aligned), eight splits' loads in flight at once; C is
+// written with one vector store when its rows allow.
 template <typename T>
-__device__ __forceinline__ void reduce_group16(const GemmParams &p, int64_t row, int c0)
+__device__ __forceinline__ void reduce_group4(const GemmParams &p, int64_t row, int c0)
 {
-    typedef T V8 __attribute__((ext_vector_type(8)));
+    typedef T V4 __attribute__((ext_vector_type(4)));
     const int64_t mn = (int64_t)p.M * p.N;
-    const float *wrow = p.ws + row * p.N;
-    float acc[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    const bool full = c0 + 16 <= p.N;
+    const float *wcol = p.ws + row * p.N + c0;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool full = c0 + 4 <= p.N;
     if (full && (p.N & 3) == 0) {
-        int sp = 0;
-        for (; sp + 4 <= p.splits; sp += 4) {
-            f32x4 x[4][4];
+        for (int sp = 0; sp < p.splits; sp += 8) {
+            // up to eight loads issued before the in-order sums
+            f32x4 x[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 8; ++u)
+                if (sp + u < p.splits) x[u] = *(const f32x4 *)(wcol + (sp + u) * mn);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) x[u][q] = *(const f32x4 *)(wrow + (sp + u) * mn + c0 + 4 * q);
+            for (int u = 0; u < 8; ++u)
+                if (sp + u < p.splits)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[4 * q + e] += x[u][q][e];
-        }
-        for (; sp < p.splits; ++sp) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 x = *(const f32x4 *)(wrow + sp * mn + c0 + 4 * q);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[4 * q + e] += x[e];
-            }
+                    for (int e = 0; e < 4; ++e) acc[e] += x[u][e];
         }
     } else {
         for (int sp = 0; sp < p.splits; ++sp)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (c0 + e < p.N) acc[e] += wrow[sp * mn + c0 + e];
+            for (int e = 0; e < 4; ++e)
+                if (c0 + e < p.N) acc[e] += wcol[sp * mn + e];
     }
     T *c = (T *)p.C + row * p.ldc + c0;
     if (full && p.c_vec) {
-        float cin[16];
+        // rows start on 16-byte boundaries and c0 is a multiple of 4
+        float cin[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.beta != 0.f) {
+            const V4 ci = *(const V4 *)c;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) cin[e] = 0.f;
-        if constexpr (sizeof(T) == 2) {
-            if (p.beta != 0.f) {
-                const V8 c0v = *(const V8 *)c, c1v = *(const V8 *)(c + 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    cin[e] = (float)c0v[e];
-                    cin[8 + e] = (float)c1v[e];
-                }
-            }
-            epilogue_row16<T>(p, acc, cin, c0);
-            V8 o0, o1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o0[e] = (T)acc[e];
-                o1[e] = (T)acc[8 + e];
-            }
-            *(V8 *)c = o0;
-            *(V8 *)(c + 8) = o1;
-        } else {
-            if (p.beta != 0.f) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 x = *(const f32x4 *)(c + 4 * q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cin[4 * q + e] = x[e];
-                }
-            }
-            epilogue_row16<T>(p, acc, cin, c0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *(f32x4 *)(c + 4 * q) = (f32x4){acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            for (int e = 0; e < 4; ++e) cin[e] = (float)ci[e];
         }
+        epilogue_row<T, 4>(p, acc, cin, c0);
+        V4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (T)acc[e];
+        *(V4 *)c = o;
     } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < 4; ++e) {
             if (c0 + e < p.N) {
                 const float cin = p.beta != 0.f ? (float)c[e] : 0.f;
                 c[e] = (T)epilogue_value<T>(p, acc[e], cin, c0 + e);

@@ -123,8 +123,8 @@ __global__ __launch_bounds__(256) void scale_c_kernel(GemmParams p)
 
 // Split-K reduction (the second kernel of dg_gemm_splitk): C =
 // act(alpha * sum_s ws[s] + beta * C + bias), the splits summed in increasing
-// s (reduce_group16).  A thread takes 16 consecutive columns of one row; a
-// row has 2^tpr_log2 threads (enough to cover N / 16 groups, at most 256), a
+// s (reduce_group4).  A thread takes 4 consecutive columns of one row; a row
+// has 2^tpr_log2 threads (enough to cover N / 4 groups, at most 256), a
 // workgroup 256 >> tpr_log2 rows, so the row and column come from shifts.
 template <typename T>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int tpr_log2)
@@ -132,13 +132,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int tp
     const int tpr = 1 << tpr_log2;
     const int64_t row = (int64_t)blockIdx.x * (256 >> tpr_log2) + (threadIdx.x >> tpr_log2);
     if (row >= p.M) return;
-    for (int c0 = (threadIdx.x & (tpr - 1)) * 16; c0 < p.N; c0 += tpr * 16) reduce_group16<T>(p, row, c0);
+    for (int c0 = (threadIdx.x & (tpr - 1)) * 4; c0 < p.N; c0 += tpr * 4) reduce_group4<T>(p, row, c0);
 }
 
 template <typename T>
 hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t s)
 {
-    const int64_t groups = ((int64_t)p.N + 15) / 16;          // 16-column groups per row
+    const int64_t groups = ((int64_t)p.N + 3) / 4;            // 4-column groups per row
     int tpr_log2 = 0;
     while (tpr_log2 < 8 && ((int64_t)1 << tpr_log2) < groups) ++tpr_log2;
     const int64_t rows_per_block = 256 >> tpr_log2;
