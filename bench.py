@@ -5,9 +5,18 @@
 A step is one C = A @ B in fp32, M = N = K = 4096, row-major, not transposed,
 A and B iid uniform[-1, 1) (seed 1), already resident in device memory; the
 timed region is exactly K steps on one stream, bracketed by device
-synchronisation.  Also measured (same method, extra keys of the one JSON
-line): fp16 operands / fp32 accumulation / fp16 output at 2048^3 in the nn,
-tn and nt variants (entries N(0,1)/sqrt(K) rounded to fp16, seed 2).
+synchronisation, after W untimed steps (and at least 100 ms of them).  Every
+input is generated and uploaded before the first timed launch.
+
+Also measured (same method, extra keys of the one JSON line), each with every
+output of a timed call checked against the CPU oracle:
+  fp16_2048 / bf16_2048  16-bit operands, fp32 accumulation, 16-bit output at
+                         2048^3, nn/tn/nt (entries N(0,1)/sqrt(K), seed 2);
+  sgemm_512              SGEMM 512^3 nn (uniform, seed 0);
+  sgemm_ragged           C = 1.5 op(A) op(B) - 0.5 C at 4095x4097x1031 and
+                         8192x256x8192, four transpose pairs, ld + 8 (seed 4);
+  attention_heads, epilogue, lora_step  the strided-batch, fused-epilogue and
+                         LoRA-step workloads (timings).
 
 `roofline` is for the fp32 kernel: achieved TFLOP/s = 2*M*N*K per launch /
 mean launch duration, timed with events recorded on the stream the kernel runs
@@ -16,8 +25,8 @@ matrix-core rate the control probe measures on the same box.  `control` holds
 the control benchmarks (matrix-core peak with the shader clock under load, and
 a plain copy) and whether they are within 10% of their references;
 `per_launch_us` and `cold_us` give per-launch medians, best and worst, and the
-median after a 512 MiB cache scrub.  `cpu_baseline`
-times the CPU oracle (plain fp64 triple loop, all host cores) on a bounded
+median after a 512 MiB cache scrub.  `cpu_baseline` times the CPU oracle
+(plain fp64 triple loop, the host cores this process may use) on a bounded
 sample of the same workload: whole rows of C.
 """
 from __future__ import annotations
@@ -44,6 +53,12 @@ REF_MFMA_F32 = PEAK_F32
 REF_MFMA_F16 = PEAK_F16
 REF_COPY_GBS = 4600.0
 CONTROL_TOL = 0.10
+
+# What `traffic` counts: bytes the L2 caches exchange with the memory fabric
+# per launch (read requests by size + write requests by size, from rocprofv3
+# TCC_EA0 counters).  The 256 MB Infinity Cache sits behind that interface, so
+# its hits are included: the figure is an upper bound on HBM traffic.
+TRAFFIC_SOURCE = "L2-to-fabric bytes per launch (TCC_EA0 read/write requests x request size; includes Infinity Cache hits)"
 
 
 def tflops(M, N, K, seconds):
@@ -92,6 +107,41 @@ def time_launches(fn, stream, reps):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / 1e3 / reps
+
+
+def warm(fn, min_count=10, min_s=0.1):
+    """Untimed launches of fn until at least min_count have run and at least
+    min_s seconds have passed (the shader clock ramps up under sustained
+    load; a few launches after an idle gap run slow).  Returns the count."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_count or time.perf_counter() - t0 < min_s:
+        for _ in range(max(1, min_count)):
+            fn()
+        n += max(1, min_count)
+        torch.cuda.synchronize()
+    return n
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_check(dtype, got, ref, ab, alpha=1.0, beta=0.0, c0=None):
+    """Every output of a timed launch against the CPU oracle: max err/bound
+    and the number of violations."""
+    import oracle
+    worst, bad = oracle.compare(dtype, got, ref, ab, alpha, beta, c0)
+    return {"outputs": int(got.size), "max_err_over_bound": round(worst, 4), "violations": bad}
 
 
 def per_launch(fn, stream, n):
@@ -266,9 +316,10 @@ def _dev_tensor(x, dtype, dev):
     return torch.from_numpy(x).to(dev)
 
 
-def bf16_square(dev, stream, reps):
+def bf16_square(dev, stream, reps, check=True):
     """bf16 operands, fp32 accumulation, bf16 output at 2048^3, nn/tn/nt, with
-    the fp16 workload's recipe (N(0,1)/sqrt(K), seed 2)."""
+    the fp16 workload's recipe (N(0,1)/sqrt(K), seed 2); every output of the
+    timed calls against the oracle."""
     import torch
 
     import dense_gemm_amd as dg
@@ -276,6 +327,7 @@ def bf16_square(dev, stream, reps):
     S = 2048
     a, b, _ = synth.problem(S, S, S, "bf16", "normal_sqrtk", 2)
     res = {"peak": PEAK_F16, "unit": "TFLOP/s"}
+    outs = {}
     for name, ta, tb in (("nn", 0, 0), ("tn", 1, 0), ("nt", 0, 1)):
         A = _dev_tensor(a.T if ta else a, "bf16", dev)
         B = _dev_tensor(b.T if tb else b, "bf16", dev)
@@ -289,13 +341,18 @@ def bf16_square(dev, stream, reps):
             if rc != 0:
                 raise dg.GemmError(rc)
 
-        for _ in range(20):
-            f()
-        torch.cuda.synchronize()
+        warm(f, 20, 0.1)
         t = min(time_launches(f, stream, reps) for _ in range(3))
         ach = tflops(S, S, S, t)
         res[name] = {"tflops": round(ach, 2), "frac": round(ach / PEAK_F16, 4),
                      "kernel_us": round(t * 1e6, 2), "kernel": dg.dg_kernel_name(k)}
+        torch.cuda.synchronize()
+        outs[name] = C.float().cpu().numpy()
+    if check:
+        import oracle
+        ref, ab = oracle.gemm(False, False, S, S, S, 1.0, a, S, b, S, 0.0, None, S)
+        for name in outs:
+            res[name]["parity"] = oracle_check("bf16", outs[name], ref, ab)
     return res
 
 
@@ -372,6 +429,89 @@ def epilogue_cost(dev, stream, reps):
     return res
 
 
+def sgemm_512(dev, stream, reps):
+    """SGEMM 512^3 nn, fp32, uniform[-1, 1) (seed 0): one launch's time, its
+    fraction of the fp32 matrix peak, and every output against the oracle."""
+    import torch
+
+    import dense_gemm_amd as dg
+    import oracle
+    import synth
+    S = 512
+    a, b, _ = synth.problem(S, S, S, "f32", "uniform", 0)
+    A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    C = torch.empty((S, S), dtype=torch.float32, device=dev)
+    k = dg.dg_select_kernel(0, 0, S, S, S, A.data_ptr(), S, B.data_ptr(), S, C.data_ptr(), S, dg.DG_F32)
+
+    def f():
+        rc = dg.dg_gemm(0, 0, S, S, S, 1.0, A.data_ptr(), S, B.data_ptr(), S, 0.0, C.data_ptr(), S,
+                        dg.DG_F32, stream.cuda_stream)
+        if rc != 0:
+            raise dg.GemmError(rc)
+
+    warm(f, 20)
+    t = min(time_launches(f, stream, reps) for _ in range(3))
+    ach = tflops(S, S, S, t)
+    ref, ab = oracle.gemm(False, False, S, S, S, 1.0, a, S, b, S, 0.0, None, S)
+    return {"workload": "SGEMM fp32 nn M=N=K=512 alpha=1 beta=0", "kernel": dg.dg_kernel_name(k),
+            "kernel_us": round(t * 1e6, 2), "tflops": round(ach, 2), "frac": round(ach / PEAK_F32, 4),
+            "per_launch_us": per_launch(f, stream, 50),
+            "parity": oracle_check("f32", C.cpu().numpy(), ref, ab)}
+
+
+def sgemm_ragged(dev, stream, reps):
+    """The fp32 full-form workloads: C = 1.5 op(A) op(B) - 0.5 C with M, N, K
+    = 4095, 4097, 1031 and 8192, 256, 8192, all four transpose pairs, every
+    row stride padded by 8 (NaN in the padding), uniform[-1, 1) (seed 4).
+    Per variant: the kernel, its time and fraction of the fp32 peak, and every
+    output of one call from C0 against the oracle (one oracle run per shape:
+    the variants share their logical operands)."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_amd as dg
+    import oracle
+    import synth
+    alpha, beta = 1.5, -0.5
+    out = {}
+    for M, N, K in ((4095, 4097, 1031), (8192, 256, 8192)):
+        a, b, c0 = synth.problem(M, N, K, "f32", "uniform", 4, with_c0=True)
+        C0, ldc = synth.store(c0, False, N + 8)
+        ref, ab = oracle.gemm(False, False, M, N, K, alpha, np.ascontiguousarray(a), K,
+                              np.ascontiguousarray(b), N, beta, c0, N)
+        res = {}
+        for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            sa, lda = synth.store(a, bool(ta), (M if ta else K) + 8)
+            sb, ldb = synth.store(b, bool(tb), (K if tb else N) + 8)
+            A, B = torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev)
+            Cd = torch.from_numpy(C0).to(dev)
+            k = dg.dg_select_kernel(ta, tb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                    Cd.data_ptr(), ldc, dg.DG_F32)
+
+            def f(ta=ta, tb=tb, A=A, B=B, C=Cd, lda=lda, ldb=ldb):
+                rc = dg.dg_gemm(ta, tb, M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, beta,
+                                C.data_ptr(), ldc, dg.DG_F32, stream.cuda_stream)
+                if rc != 0:
+                    raise dg.GemmError(rc)
+
+            # one call from C0, checked; then the timed calls (which keep
+            # updating C in place: C <- 1.5 AB - 0.5 C stays bounded)
+            f()
+            torch.cuda.synchronize()
+            got = Cd.cpu().numpy()
+            parity = oracle_check("f32", got[:, :N], ref, ab, alpha, beta, c0)
+            parity["c_padding_untouched"] = bool(np.isnan(got[:, N:]).all())
+            warm(f, 5)
+            t = min(time_launches(f, stream, reps) for _ in range(3))
+            ach = tflops(M, N, K, t)
+            res[("t" if ta else "n") + ("t" if tb else "n")] = {
+                "kernel": dg.dg_kernel_name(k), "kernel_us": round(t * 1e6, 2),
+                "tflops": round(ach, 2), "frac": round(ach / PEAK_F32, 4), "parity": parity}
+            del A, B, Cd
+        out[f"{M}x{N}x{K}"] = res
+    return {"alpha": alpha, "beta": beta, "ld_pad": 8, **out}
+
+
 def smi_clocks(index=0):
     """Clock state from `amd-smi metric --clock --json` (a child process): the
     median current shader clock over the XCDs, its range, whether it is
@@ -406,8 +546,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-f16", action="store_true", help="skip the fp16 2048^3 measurements")
+    ap.add_argument("--no-f16", action="store_true", help="skip the 16-bit measurements")
     ap.add_argument("--no-lora", action="store_true", help="skip the LoRA-step GEMM sequence")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the SGEMM 512^3 and ragged full-form legs")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the oracle checks of the timed outputs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-cold", action="store_true",
@@ -433,6 +577,16 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
+    # ---- inputs: generated and resident in device memory before any timing ----
+    M = N = K = 4096
+    a, b, _ = synth.problem(M, N, K, "f32", "uniform", 1)
+    A = torch.from_numpy(a).to(dev)
+    B = torch.from_numpy(b).to(dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    S = 2048
+    a16, b16, _ = (None, None, None) if args.no_f16 else synth.problem(S, S, S, "f16", "normal_sqrtk", 2)
+    torch.cuda.synchronize()
+
     smi_before = smi_clocks()
     control = control_probes(dev, stream)
 
@@ -444,12 +598,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- fp32 4096^3 nn ---------------------------------------------------
-    M = N = K = 4096
-    a, b, _ = synth.problem(M, N, K, "f32", "uniform", 1)
-    A = torch.from_numpy(a).to(dev)
-    B = torch.from_numpy(b).to(dev)
-    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # ---- fp32 4096^3 nn: the step ------------------------------------------------
     kernel = dg.dg_select_kernel(0, 0, M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N,
                                  dg.DG_F32)
 
@@ -459,8 +608,9 @@ def main():
         if rc != 0:
             raise dg.GemmError(rc)
 
-    for _ in range(args.warmup):
-        step()
+    # W untimed steps, and at least 100 ms of them (the control probes above
+    # keep the GPU busy up to here; the clock still settles under this load)
+    warmup_launches = warm(step, args.warmup, 0.1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     launch_s = time_launches(step, stream, args.steps)
@@ -481,6 +631,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_launches": warmup_launches,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -492,6 +643,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_F32,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32, 4),
                      "traffic": measured_traffic(kernel, 0, 0, M, N),
+                     "traffic_source": TRAFFIC_SOURCE,
                      "algorithmic_bytes": 3 * M * N * 4, "kernel_ms": round(launch_s * 1e3, 4),
                      "frac_of_probe_peak": round(achieved / control["mfma_f32_tflops"], 4),
                      "probe_clock_mhz": control["mfma_f32_clock_mhz"]},
@@ -506,9 +658,8 @@ def main():
 
     # ---- fp16 2048^3 nn / tn / nt ---------------------------------------------
     if not args.no_f16:
-        S = 2048
-        a16, b16, _ = synth.problem(S, S, S, "f16", "normal_sqrtk", 2)
         res = {}
+        outs = {}
         for name, ta, tb in (("nn", 0, 0), ("tn", 1, 0), ("nt", 0, 1)):
             As = torch.from_numpy(np.ascontiguousarray(a16.T if ta else a16)).to(dev)
             Bs = torch.from_numpy(np.ascontiguousarray(b16.T if tb else b16)).to(dev)
@@ -522,9 +673,7 @@ def main():
                 if rc != 0:
                     raise dg.GemmError(rc)
 
-            for _ in range(20):
-                step16()
-            torch.cuda.synchronize()
+            warm(step16, 20, 0.1)
             reps = max(args.steps, 200)
             t16 = min(time_launches(step16, stream, reps) for _ in range(3))
             ach = tflops(S, S, S, t16)
@@ -535,11 +684,27 @@ def main():
                          "algorithmic_bytes": 3 * S * S * 2,
                          "per_launch_us": per_launch(step16, stream, 100),
                          "cold_us": None if args.no_cold else cold_launches(step16, stream, 20, scrub)}
+            torch.cuda.synchronize()
+            outs[name] = Cs.float().cpu().numpy()
+            del As, Bs, Cs
+        if not args.no_check:
+            # the variants share their logical operands: one oracle run
+            import oracle
+            ref, ab = oracle.gemm(False, False, S, S, S, 1.0, a16, S, b16, S, 0.0, None, S)
+            for name in outs:
+                res[name]["parity"] = oracle_check("f16", outs[name], ref, ab)
+            del ref, ab
         out["fp16_2048"] = {"peak": PEAK_F16, "unit": "TFLOP/s", **res}
+        del outs
 
     # ---- bf16 2048^3 nn / tn / nt (same recipe as fp16) ------------------------
     if not args.no_f16:
-        out["bf16_2048"] = bf16_square(dev, stream, max(args.steps, 200))
+        out["bf16_2048"] = bf16_square(dev, stream, max(args.steps, 200), not args.no_check)
+
+    # ---- SGEMM 512^3 and the ragged full-form workloads -------------------------
+    if not args.no_extra:
+        out["sgemm_512"] = sgemm_512(dev, stream, max(args.steps, 200))
+        out["sgemm_ragged"] = sgemm_ragged(dev, stream, max(args.steps // 2, 10))
 
     # ---- attention per-head products (strided batch over heads) ----------------
     if not args.no_f16:
@@ -556,8 +721,7 @@ def main():
     # ---- CPU baseline: the oracle on whole rows of the same problem -------------
     if not args.no_cpu:
         import oracle
-        cores = len(os.sched_getaffinity(0))
-        cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+        cores = oracle.default_threads()
 
         def oracle_rows(nrows):
             t = time.perf_counter()
@@ -572,7 +736,7 @@ def main():
         worst, bad = oracle.compare("f32", got, ref, ab, 1.0, 0.0)
         flops = 2.0 * nrows * N * K
         out["cpu_baseline"] = {"value": round(flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": cores, "kind": "oracle",
+                               "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
                                "sample": f"rows 0..{nrows - 1} of C (all {N} columns, K={K}), "
                                          f"{t_cpu:.1f} s",
                                "sample_max_err_over_bound": round(worst, 4),

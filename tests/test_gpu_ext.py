@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import Batched, Problem, check_full, check_sampled
+from gpu_util import Batched, Problem, check_full
 
 pytestmark = pytest.mark.gpu
 TRANS = list(itertools.product([False, True], [False, True]))
@@ -42,11 +42,12 @@ def bias_for(N, dtype, seed, scale=1.0):
 # bf16
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True)])
-def test_bf16_2048_sampled(dg, ta, tb):
+def test_bf16_2048_full(dg, ta, tb):
     """The fp16 headline workload's recipe (N(0,1)/sqrt(K), seed 2) in bf16."""
     S = 2048
     a, b, _ = synth.problem(S, S, S, "bf16", "normal_sqrtk", 2)
-    check_sampled(Problem(a, b, None, ta, tb, 1.0, 0.0, "bf16"), n=3000, seed=9)
+    worst = check_full(Problem(a, b, None, ta, tb, 1.0, 0.0, "bf16"))
+    print(f"bf16 2048^3 ta={ta} tb={tb}: max err/bound {worst:.4f}", flush=True)
 
 
 def test_bf16_output_rounding_is_rne(dg):
@@ -141,16 +142,16 @@ def test_activation_over_a_dense_range(dg, dtype, act, kernel_kind):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_epilogue_mlp_projection_sampled(dg, dtype):
+def test_epilogue_mlp_projection_full(dg, dtype):
     """The LoRA block's up-projection shape (512 x 5632 x 2048, nt) with a
-    bias and gelu fused, sampled."""
+    bias and gelu fused, every output against the oracle."""
     M, N, K = 512, 5632, 2048
     st = synth.Stream(220)
     a = synth.round_to(st.normal((M, K), 1.0), dtype)
     b = synth.round_to(st.normal((K, N), 0.02), dtype)
     bias = synth.round_to(st.normal((N,), 0.5), dtype)
     p = Problem(a, b, None, False, True, 1.0, 0.0, dtype, bias=bias, act="gelu")
-    check_sampled(p, n=3000, seed=11)
+    check_full(p)
 
 
 def test_epilogue_relu_integer_exact(dg):

@@ -342,6 +342,109 @@ def test_compare_flags_nan_and_outliers():
     assert bad == 2
 
 
+def _adjacent_pairs(dtype):
+    """Every pair of adjacent non-negative finite values of a 16-bit format,
+    decoded from consecutive bit patterns (fp16 by numpy, bf16 as the upper
+    half of an fp32 encoding)."""
+    if dtype == "f16":
+        v = np.arange(0, 0x7c00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    else:
+        bits = np.arange(0, 0x7f80, dtype=np.uint32) << np.uint32(16)
+        v = bits.view(np.float32).astype(np.float64)
+    return v[:-1], v[1:]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_half_ulp_is_half_the_gap_at_every_midpoint(dtype):
+    """The output-rounding allowance equals the largest rounding error of its
+    binade: at the midpoint of every two adjacent values (a tie, the worst
+    case) it is exactly half their gap.  A function that took the spacing of
+    the rounded value would be twice too large at the top of each binade."""
+    lo, hi = _adjacent_pairs(dtype)
+    mid = (lo + hi) / 2
+    h = oracle.half_ulp_out(dtype, mid)
+    assert np.array_equal(h, (hi - lo) / 2)
+    # inside a binade every point's allowance covers its distance to the
+    # nearest value
+    inner = lo + (hi - lo) * 0.3
+    assert np.all(oracle.half_ulp_out(dtype, inner) >= (inner - lo))
+
+
+def test_half_ulp_f16_binade_tops():
+    h = oracle.half_ulp_f16(np.array([2047.5, 2048.0, 1023.75, 1024.0, 65504.0, 65519.99, 65520.0,
+                                      2.0 ** -20, 2.0 ** -14, 2.0 ** -13]))
+    assert list(h[:6]) == [0.5, 1.0, 0.25, 0.5, 16.0, 16.0]
+    assert np.isinf(h[6])
+    assert list(h[7:]) == [2.0 ** -25, 2.0 ** -25, 2.0 ** -24]
+    # a tie below 2048 moves to 2048 by 0.5; the allowance there is 0.5, not 1
+    assert float(np.float16(2047.5)) == 2048.0
+
+
+def test_overflow_thresholds_match_rounding():
+    """Round-to-nearest-even gives an infinity exactly from the thresholds
+    on (numpy's conversions as the independent reference)."""
+    t16 = oracle.OVERFLOW["f16"]
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float16(t16)) and np.float16(np.nextafter(t16, 0)) == 65504.0
+    t32 = oracle.OVERFLOW["f32"]
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(t32))
+    assert np.float32(np.nextafter(t32, 0)) == np.finfo(np.float32).max
+    # bf16: the tie at the threshold rounds to the even neighbour, the infinity
+    tb = oracle.OVERFLOW["bf16"]
+    top = np.array([0x7f7f0000], dtype=np.uint32).view(np.float32)[0]
+    assert float(top) == oracle.BF16_MAX
+    assert tb - oracle.BF16_MAX == (2.0 ** 128 - oracle.BF16_MAX) / 2
+
+
+def test_compare_infinities():
+    """An infinite output passes only where the reference can overflow the
+    output type, with the reference's sign; a finite output where the
+    reference overflows fails; an infinite output of a small reference
+    fails."""
+    one = np.ones(1)
+    cmp = oracle.compare
+    # f16: reference beyond the threshold
+    assert cmp("f16", [np.inf], [70000.0], one, 1.0, 0.0)[1] == 0
+    assert cmp("f16", [-np.inf], [70000.0], one, 1.0, 0.0)[1] == 1
+    assert cmp("f16", [65504.0], [70000.0], one, 1.0, 0.0)[1] == 1
+    assert cmp("f16", [-np.inf], [-70000.0], one, 1.0, 0.0)[1] == 0
+    # f16: just below the threshold, no overflow possible
+    assert cmp("f16", [np.inf], [65519.0], one, 1.0, 0.0)[1] == 1
+    assert cmp("f16", [65504.0], [65519.0], one, 1.0, 0.0)[1] == 0
+    # f16: within bound_pre of the threshold: either neighbour is a correct rounding
+    ab = np.array([5000.0])                   # bound_pre = 2e-3 * 5000 + 1e-4 = 10.0001
+    assert cmp("f16", [np.inf], [65515.0], ab, 1.0, 0.0)[1] == 0
+    assert cmp("f16", [65504.0], [65515.0], ab, 1.0, 0.0)[1] == 0
+    # an infinity where the reference is small
+    assert cmp("f16", [np.inf], [100.0], one, 1.0, 0.0)[1] == 1
+    assert cmp("f32", [np.inf], [1e38], one, 1.0, 0.0)[1] == 1
+    assert cmp("f16o32", [np.inf], [70000.0], one, 1.0, 0.0)[1] == 1   # fp32 output holds 70000
+    # fp32 and bf16 overflow
+    assert cmp("f32", [np.inf], [3.5e38], one, 1.0, 0.0)[1] == 0
+    assert cmp("f32", [-np.inf], [3.5e38], one, 1.0, 0.0)[1] == 1
+    assert cmp("bf16", [-np.inf], [-4e38], one, 1.0, 0.0)[1] == 0
+    assert cmp("bf16", [np.inf], [-4e38], one, 1.0, 0.0)[1] == 1
+    # an infinite reference
+    assert cmp("f32", [np.inf], [np.inf], one, 1.0, 0.0)[1] == 0
+    assert cmp("f32", [1.0], [np.inf], one, 1.0, 0.0)[1] == 1
+    assert cmp("f32", [np.nan], [np.inf], one, 1.0, 0.0)[1] == 1
+
+
+def test_compare_binade_crossing_and_fp32_output():
+    """The output rounding is allowed at the far end of bound_pre: an
+    unrounded result just past 2048 rounds with spacing 2."""
+    ab = np.array([100.0])                    # bound_pre = 0.2001
+    assert oracle.compare("f16", [2048.0], [2047.9], ab, 1.0, 0.0)[1] == 0
+    assert oracle.compare("f16", [2050.0], [2047.9], ab, 1.0, 0.0)[1] == 1
+    # 16-bit operands with an fp32 output: no 16-bit rounding is allowed
+    z = np.zeros(1)
+    assert oracle.compare("f16", [1000.5], [1000.3], z, 1.0, 0.0)[1] == 0   # half ulp 0.25
+    assert oracle.compare("f16o32", [1000.5], [1000.3], z, 1.0, 0.0)[1] == 1
+    assert oracle.compare("f16o32", [1000.3 + 5e-5], [1000.3], z, 1.0, 0.0)[1] == 0
+    assert oracle.compare("bf16o32", [1000.3 + 2e-4], [1000.3], z, 1.0, 0.0)[1] == 1
+
+
 # ---------------------------------------------------------------------------
 # the LoRA workload recipe against the page's figures
 # ---------------------------------------------------------------------------
