@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdense_gemm_amd.so")
 
 DG_OP_N, DG_OP_T = 0, 1
-DG_F32, DG_F16_F32ACC, DG_BF16_F32ACC = 0, 1, 2
+DG_F32, DG_F16_F32ACC, DG_BF16_F32ACC, DG_F16_F32OUT, DG_BF16_F32OUT = 0, 1, 2, 3, 4
 DG_EPI_NONE, DG_EPI_RELU, DG_EPI_GELU = 0, 1, 2
 EPILOGUES = {"none": DG_EPI_NONE, "relu": DG_EPI_RELU, "gelu": DG_EPI_GELU}
 DG_OK, DG_ERR_UNSUPPORTED, DG_ERR_HIP = 0, -100, -200
@@ -176,12 +176,19 @@ def kernel_names() -> list[str]:
 
 
 # ---- torch convenience -------------------------------------------------------
-def _dtype_code(t):
+def _dtype_code(ab, c):
+    """The library's dtype for operands of torch dtype `ab` and an output of
+    torch dtype `c`: the operand type itself, or fp32 for 16-bit operands."""
     import torch
-    codes = {torch.float32: DG_F32, torch.float16: DG_F16_F32ACC, torch.bfloat16: DG_BF16_F32ACC}
-    if t.dtype not in codes:
-        raise TypeError(f"unsupported dtype {t.dtype} (float32, float16 or bfloat16)")
-    return codes[t.dtype]
+    codes = {(torch.float32, torch.float32): DG_F32,
+             (torch.float16, torch.float16): DG_F16_F32ACC,
+             (torch.bfloat16, torch.bfloat16): DG_BF16_F32ACC,
+             (torch.float16, torch.float32): DG_F16_F32OUT,
+             (torch.bfloat16, torch.float32): DG_BF16_F32OUT}
+    if (ab, c) not in codes:
+        raise TypeError(f"unsupported operand/output dtypes {ab}/{c} (float32, float16 or "
+                        "bfloat16 operands; an output of the operand dtype, or float32)")
+    return codes[(ab, c)]
 
 
 def _ld(t, name):
@@ -201,22 +208,25 @@ def _batch_stride(t, batch, name):
 
 
 def gemm(A, B, C=None, transA=False, transB=False, alpha=1.0, beta=0.0, bias=None,
-         activation="none", kernel=DG_KERNEL_AUTO, stream=None):
+         activation="none", kernel=DG_KERNEL_AUTO, stream=None, out_dtype=None):
     """C = act(alpha * op(A) @ op(B) + beta * C + bias) on torch CUDA (HIP)
     tensors, for one matrix or a strided batch.
 
     A is [M, K] (or [K, M] with transA), B is [K, N] (or [N, K] with transB);
     either may carry a leading batch dimension (a 2-D operand is shared by
     every batch); all row-major with unit column stride, ld from the row
-    stride.  bias (optional) has N elements of C's dtype; activation is
-    "none", "relu" or "gelu".  C is allocated (uninitialised, so beta must be
-    0) when None.  Runs on the current torch stream unless `stream` (a torch
-    stream) is given."""
+    stride.  A and B share one dtype; C has that dtype or, for 16-bit
+    operands, float32 (`out_dtype` picks it when C is allocated here).  bias
+    (optional) has N elements of C's dtype; activation is "none", "relu" or
+    "gelu".  C is allocated (uninitialised, so beta must be 0) when None.
+    Runs on the current torch stream unless `stream` (a torch stream) is
+    given."""
     import torch
-    dt = _dtype_code(A)
-    if B.dtype != A.dtype or (C is not None and C.dtype != A.dtype):
-        raise TypeError("A, B and C must share one dtype")
-    if bias is not None and (bias.dtype != A.dtype or bias.dim() != 1 or bias.stride(0) != 1):
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must share one dtype")
+    cdt = C.dtype if C is not None else (out_dtype if out_dtype is not None else A.dtype)
+    dt = _dtype_code(A.dtype, cdt)
+    if bias is not None and (bias.dtype != cdt or bias.dim() != 1 or bias.stride(0) != 1):
         raise TypeError("bias must be a contiguous 1-D tensor of C's dtype")
     batched = A.dim() == 3 or B.dim() == 3 or (C is not None and C.dim() == 3)
     batch = max(A.shape[0] if A.dim() == 3 else 1, B.shape[0] if B.dim() == 3 else 1,
@@ -230,7 +240,7 @@ def gemm(A, B, C=None, transA=False, transB=False, alpha=1.0, beta=0.0, bias=Non
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
-        C = torch.empty((batch, M, N) if batched else (M, N), dtype=A.dtype, device=A.device)
+        C = torch.empty((batch, M, N) if batched else (M, N), dtype=cdt, device=A.device)
     if tuple(C.shape[-2:]) != (M, N) or (batched and (C.dim() != 3 or C.shape[0] != batch)):
         raise ValueError(f"C must be [{batch}, {M}, {N}]" if batched else f"C must be [{M}, {N}]")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)

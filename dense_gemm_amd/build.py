@@ -21,11 +21,12 @@ LIB = os.path.join(PKG, "libdense_gemm_amd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gemm_simple.hip", "gemm_f32.hip", "gemm_f16.hip", "gemm_bf16.hip"]
+SOURCES = ["api.cpp", "gemm_simple.hip", "gemm_f32.hip", "gemm_f16.hip", "gemm_bf16.hip",
+           "gemm_f16_o32.hip", "gemm_bf16_o32.hip"]
 # the control probes of the measurements, a library of their own
 PROBE_LIB = os.path.join(PKG, "libdense_gemm_probe.so")
 PROBE_SOURCES = ["probe.hip"]
-HEADERS = ["gemm_common.hpp", "gemm_mfma.hpp", "gemm_pipe.hpp"]
+HEADERS = ["gemm_common.hpp", "gemm_mfma.hpp", "gemm_pipe.hpp", "gemm_tables16.hpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -18,6 +18,10 @@ const launch_fn *f16_pipe_launchers(int config);
 const launch_fn *f32_pipe_launchers(int config);
 const launch_fn *bf16_pipe_launchers(int config);
 const launch_fn *bf16_launchers(int config);
+const launch_fn *f16_o32_launchers(int config);
+const launch_fn *f16_o32_pipe_launchers(int config);
+const launch_fn *bf16_o32_launchers(int config);
+const launch_fn *bf16_o32_pipe_launchers(int config);
 }  // namespace dg
 
 namespace {
@@ -37,6 +41,9 @@ thread_local int g_last_hip_error = 0;
 //   PIPE_DW: fp32 pipelined kernels with 4-byte direct loads; any fp32
 //           layout (4-byte aligned A and B).
 //   Both pipelined kinds address a tile's operands with 32-bit byte offsets.
+// `dtype` is the operand type (DG_F32, DG_F16_F32ACC or DG_BF16_F32ACC); a
+// 16-bit family serves both of its output types: `variants` writes C in the
+// operand type, `variants32` the same kernels writing an fp32 C.
 enum Kind { SIMPLE, MFMA, PIPE, PIPE_DW };
 struct Family {
     const char *name;
@@ -46,6 +53,7 @@ struct Family {
     Kind kind;
     const launch_fn *(*variants)(int);
     int config;
+    const launch_fn *(*variants32)(int);
 };
 
 const Family kFamilies[] = {
@@ -53,34 +61,38 @@ const Family kFamilies[] = {
     {"f16_64x64_simple", DG_F16_F32ACC, 64, 64, 1, SIMPLE, nullptr, 0},
     {"f32_256x128_mfma32x32x2", DG_F32, 256, 128, 8, MFMA, dg::f32_launchers, 0},
     {"f32_128x128_mfma32x32x2", DG_F32, 128, 128, 8, MFMA, dg::f32_launchers, 1},
-    {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, MFMA, dg::f16_launchers, 0},
-    {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, MFMA, dg::f16_launchers, 1},
-    {"f16_128x128_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0},
-    {"f16_256x128_pipe3_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1},
-    {"f16_128x128_pipe2_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 2},
+    {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, MFMA, dg::f16_launchers, 0, dg::f16_o32_launchers},
+    {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, MFMA, dg::f16_launchers, 1, dg::f16_o32_launchers},
+    {"f16_128x128_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0, dg::f16_o32_pipe_launchers},
+    {"f16_256x128_pipe3_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1, dg::f16_o32_pipe_launchers},
+    {"f16_128x128_pipe2_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 2, dg::f16_o32_pipe_launchers},
     {"f32_256x128_pipe3_mfma32x32x2", DG_F32, 256, 128, 8, PIPE, dg::f32_pipe_launchers, 0},
     {"f32_256x256_pipe4_w8_mfma32x32x2", DG_F32, 256, 256, 4, PIPE, dg::f32_pipe_launchers, 1},
     {"f32_128x128_pipe4_mfma32x32x2", DG_F32, 128, 128, 8, PIPE, dg::f32_pipe_launchers, 2},
     {"bf16_64x64_simple", DG_BF16_F32ACC, 64, 64, 1, SIMPLE, nullptr, 0},
-    {"bf16_128x128_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 0},
-    {"bf16_256x128_pipe3_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1},
-    {"bf16_128x128_pipe2_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 2},
-    {"f16_64x64_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE, dg::f16_pipe_launchers, 3},
-    {"f16_128x32_pipe4_mfma32x32x16", DG_F16_F32ACC, 128, 32, 4, PIPE, dg::f16_pipe_launchers, 4},
-    {"f16_32x128_pipe4_mfma32x32x16", DG_F16_F32ACC, 32, 128, 4, PIPE, dg::f16_pipe_launchers, 5},
-    {"bf16_64x64_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE, dg::bf16_pipe_launchers, 3},
-    {"bf16_128x32_pipe4_mfma32x32x16", DG_BF16_F32ACC, 128, 32, 4, PIPE, dg::bf16_pipe_launchers, 4},
-    {"bf16_32x128_pipe4_mfma32x32x16", DG_BF16_F32ACC, 32, 128, 4, PIPE, dg::bf16_pipe_launchers, 5},
-    {"f16_256x256_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 256, 4, PIPE, dg::f16_pipe_launchers, 6},
-    {"bf16_256x256_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 256, 4, PIPE, dg::bf16_pipe_launchers, 6},
+    {"bf16_128x128_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 0, dg::bf16_o32_pipe_launchers},
+    {"bf16_256x128_pipe3_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1, dg::bf16_o32_pipe_launchers},
+    {"bf16_128x128_pipe2_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 2, dg::bf16_o32_pipe_launchers},
+    {"f16_64x64_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE, dg::f16_pipe_launchers, 3, dg::f16_o32_pipe_launchers},
+    {"f16_128x32_pipe4_mfma32x32x16", DG_F16_F32ACC, 128, 32, 4, PIPE, dg::f16_pipe_launchers, 4, dg::f16_o32_pipe_launchers},
+    {"f16_32x128_pipe4_mfma32x32x16", DG_F16_F32ACC, 32, 128, 4, PIPE, dg::f16_pipe_launchers, 5, dg::f16_o32_pipe_launchers},
+    {"bf16_64x64_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE, dg::bf16_pipe_launchers, 3, dg::bf16_o32_pipe_launchers},
+    {"bf16_128x32_pipe4_mfma32x32x16", DG_BF16_F32ACC, 128, 32, 4, PIPE, dg::bf16_pipe_launchers, 4, dg::bf16_o32_pipe_launchers},
+    {"bf16_32x128_pipe4_mfma32x32x16", DG_BF16_F32ACC, 32, 128, 4, PIPE, dg::bf16_pipe_launchers, 5, dg::bf16_o32_pipe_launchers},
+    {"f16_256x256_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 256, 4, PIPE, dg::f16_pipe_launchers, 6, dg::f16_o32_pipe_launchers},
+    {"bf16_256x256_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 256, 4, PIPE, dg::bf16_pipe_launchers, 6, dg::bf16_o32_pipe_launchers},
     {"f32_256x128_pipe3_dw_mfma32x32x2", DG_F32, 256, 128, 8, PIPE_DW, dg::f32_pipe_launchers, 3},
     {"f32_128x128_pipe4_dw_mfma32x32x2", DG_F32, 128, 128, 8, PIPE_DW, dg::f32_pipe_launchers, 4},
-    {"f16_128x128_pipe4_ksplit2_dw_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE_DW, dg::f16_pipe_launchers, 7},
-    {"f16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE_DW, dg::f16_pipe_launchers, 8},
-    {"bf16_128x128_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE_DW, dg::bf16_pipe_launchers, 7},
-    {"bf16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE_DW, dg::bf16_pipe_launchers, 8},
-    {"bf16_128x128_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, MFMA, dg::bf16_launchers, 0},
-    {"bf16_256x128_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, MFMA, dg::bf16_launchers, 1},
+    {"f16_128x128_pipe4_ksplit2_dw_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE_DW, dg::f16_pipe_launchers, 7, dg::f16_o32_pipe_launchers},
+    {"f16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE_DW, dg::f16_pipe_launchers, 8, dg::f16_o32_pipe_launchers},
+    {"bf16_128x128_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE_DW, dg::bf16_pipe_launchers, 7, dg::bf16_o32_pipe_launchers},
+    {"bf16_64x64_pipe4_ksplit2_dw_mfma32x32x16", DG_BF16_F32ACC, 64, 64, 4, PIPE_DW, dg::bf16_pipe_launchers, 8, dg::bf16_o32_pipe_launchers},
+    {"bf16_128x128_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, MFMA, dg::bf16_launchers, 0, dg::bf16_o32_launchers},
+    {"bf16_256x128_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, MFMA, dg::bf16_launchers, 1, dg::bf16_o32_launchers},
+    {"f32_128x64_pipe4_mfma32x32x2", DG_F32, 128, 64, 8, PIPE, dg::f32_pipe_launchers, 5},
+    {"f32_64x64_pipe4_mfma32x32x2", DG_F32, 64, 64, 8, PIPE, dg::f32_pipe_launchers, 6},
+    {"f32_128x64_pipe4_dw_mfma32x32x2", DG_F32, 128, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 7},
+    {"f32_64x64_pipe4_dw_mfma32x32x2", DG_F32, 64, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 8},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -91,7 +103,8 @@ enum {
     K_F16_PIPE_32x128 = 18, K_BF16_PIPE_64 = 19, K_BF16_PIPE_128x32 = 20, K_BF16_PIPE_32x128 = 21,
     K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23, K_F32_PIPE_256x128_DW = 24,
     K_F32_PIPE_128_DW = 25, K_F16_PIPE_128_DW = 26, K_F16_PIPE_64_DW = 27, K_BF16_PIPE_128_DW = 28,
-    K_BF16_PIPE_64_DW = 29, K_BF16_128 = 30, K_BF16_256 = 31
+    K_BF16_PIPE_64_DW = 29, K_BF16_128 = 30, K_BF16_256 = 31, K_F32_PIPE_128x64 = 32,
+    K_F32_PIPE_64 = 33, K_F32_PIPE_128x64_DW = 34, K_F32_PIPE_64_DW = 35
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -105,9 +118,23 @@ struct Ext {
     int act = DG_EPI_NONE;
 };
 
-bool is_dtype(int dtype) { return dtype == DG_F32 || dtype == DG_F16_F32ACC || dtype == DG_BF16_F32ACC; }
+bool is_dtype(int dtype)
+{
+    return dtype == DG_F32 || dtype == DG_F16_F32ACC || dtype == DG_BF16_F32ACC ||
+           dtype == DG_F16_F32OUT || dtype == DG_BF16_F32OUT;
+}
 
-int64_t elem_bytes(int dtype) { return dtype == DG_F32 ? 4 : 2; }
+// The operand type of a dtype (the type the kernel table is keyed by).
+int op_dtype(int dtype)
+{
+    return dtype == DG_F16_F32OUT ? DG_F16_F32ACC : dtype == DG_BF16_F32OUT ? DG_BF16_F32ACC : dtype;
+}
+
+// Bytes of one element of A and B.
+int64_t elem_bytes(int dtype) { return op_dtype(dtype) == DG_F32 ? 4 : 2; }
+
+// Bytes of one element of C (and of the bias).
+int64_t c_bytes(int dtype) { return (dtype == DG_F16_F32ACC || dtype == DG_BF16_F32ACC) ? 2 : 4; }
 
 constexpr int64_t kMaxDim = 0x7fffffff;
 
@@ -145,7 +172,7 @@ int validate_ext(int64_t M, int64_t N, int64_t ldc, const Ext &x, int dtype)
     // batches of C must not overlap: batch b+1 starts past the last element of batch b
     if (x.sC < 0 || (x.batch > 1 && M > 0 && N > 0 && x.sC < (M - 1) * ldc + N)) return -16;
     if (x.batch < 0 || x.batch > kMaxBatch) return -17;
-    if (x.bias && ((uintptr_t)x.bias % (uintptr_t)elem_bytes(dtype)) != 0) return -18;
+    if (x.bias && ((uintptr_t)x.bias % (uintptr_t)c_bytes(dtype)) != 0) return -18;
     if (x.act != DG_EPI_NONE && x.act != DG_EPI_RELU && x.act != DG_EPI_GELU) return -19;
     return 0;
 }
@@ -230,6 +257,8 @@ int dw_kernel(int k, bool bf)
 int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
            const void *B, int64_t ldb, int dtype, const Ext &x = Ext())
 {
+    // the output type does not change the choice: the kernels are the same
+    dtype = op_dtype(dtype);
     // a batch multiplies the workgroups: count the tiles of all batches
     const int64_t nb = x.batch > 1 ? x.batch : 1;
     const int64_t big = ceil_div(M, 256) * ceil_div(N, 128) * nb;
@@ -307,7 +336,7 @@ bool supports(int kernel, int ta, int tb, int64_t M, int64_t N, int64_t K, const
 {
     if (kernel < 0 || kernel >= kNumKernels) return false;
     const Family &f = kFamilies[kernel];
-    if (f.dtype != dtype) return false;
+    if (f.dtype != op_dtype(dtype)) return false;
     if (f.kind == SIMPLE) return ceil_div(M, 64) <= 65535;
     if (f.kind == PIPE && !pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x)) return false;
     if (f.kind == PIPE_DW && !pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return false;
@@ -354,7 +383,7 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     p.beta = beta;
     p.tiles_m = p.tiles_n = 0;
     p.group_m = 1;
-    const int64_t v = 16 / elem_bytes(dtype);
+    const int64_t v = 16 / c_bytes(dtype);
     p.c_vec = aligned16(C) && ldc % v == 0 && (x.batch <= 1 || x.sC % v == 0);
     p.splits = 1;
     p.k_chunk = 0;
@@ -366,7 +395,8 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     p.strideC = x.sC;
     p.batch = (int32_t)x.batch;
     hipStream_t s = (hipStream_t)stream;
-    const int di = dtype;   // launcher tables are indexed by dtype
+    const int di = dtype;   // the generic launcher tables are indexed by dtype
+    const bool out32 = dtype == DG_F16_F32OUT || dtype == DG_BF16_F32OUT;
 
     hipError_t err;
     if (K == 0 || alpha == 0.f) {
@@ -394,7 +424,7 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
                 }
             }
             const int vi = (f.kind == PIPE || f.kind == PIPE_DW || vec_ok(A, lda, B, ldb, dtype, x)) ? 0 : 4;
-            err = f.variants(f.config)[vi + ta * 2 + tb](p, s);
+            err = (out32 ? f.variants32 : f.variants)(f.config)[vi + ta * 2 + tb](p, s);
             if (err == hipSuccess && p.splits > 1) err = dg::splitk_reduce_launcher(di)(p, s);
         }
     }
@@ -409,37 +439,37 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
 
 extern "C" {
 
-int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
-            int64_t lda, const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype,
+int dg_gemm(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+            int64_t lda, const void *B, int64_t ldb, float beta, void *C, int64_t ldc, dg_dtype_t dtype,
             void *stream)
 {
     return run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
                DG_KERNEL_AUTO);
 }
 
-int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+int dg_gemm_with_kernel(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
-                        void *C, int64_t ldc, int dtype, void *stream, int kernel)
+                        void *C, int64_t ldc, dg_dtype_t dtype, void *stream, int kernel)
 {
     return run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
                kernel);
 }
 
-int dg_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+int dg_gemm_ex(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha,
                const void *A, int64_t lda, int64_t strideA, const void *B, int64_t ldb,
                int64_t strideB, float beta, void *C, int64_t ldc, int64_t strideC,
-               int64_t batch, const void *bias, int epilogue, int dtype, void *stream)
+               int64_t batch, const void *bias, dg_epilogue_t epilogue, dg_dtype_t dtype, void *stream)
 {
     return dg_gemm_ex_with_kernel(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
                                   strideB, beta, C, ldc, strideC, batch, bias, epilogue, dtype,
                                   stream, DG_KERNEL_AUTO);
 }
 
-int dg_gemm_ex_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+int dg_gemm_ex_with_kernel(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha,
                            const void *A, int64_t lda, int64_t strideA, const void *B,
                            int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc,
-                           int64_t strideC, int64_t batch, const void *bias, int epilogue,
-                           int dtype, void *stream, int kernel)
+                           int64_t strideC, int64_t batch, const void *bias,
+                           dg_epilogue_t epilogue, dg_dtype_t dtype, void *stream, int kernel)
 {
     Ext x;
     x.sA = strideA;
@@ -458,9 +488,9 @@ int dg_gemm_ex_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t
     return rc < 0 && rc > -100 ? ex_position(rc) : rc;
 }
 
-int dg_gemm_splitk(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+int dg_gemm_splitk(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha,
                    const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
-                   int64_t ldc, int dtype, void *stream, int splits, void *workspace,
+                   int64_t ldc, dg_dtype_t dtype, void *stream, int splits, void *workspace,
                    size_t workspace_bytes)
 {
     int rc = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
@@ -471,7 +501,8 @@ int dg_gemm_splitk(int transA, int transB, int64_t M, int64_t N, int64_t K, floa
                DG_KERNEL_AUTO, splits, workspace, workspace_bytes);
 }
 
-int dg_gemm_splitk_choose(int transA, int transB, int64_t M, int64_t N, int64_t K, int dtype)
+int dg_gemm_splitk_choose(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K,
+                          dg_dtype_t dtype)
 {
     int rc = validate(transA, transB, M, N, K, 1.f, nullptr, transA ? (M > 1 ? M : 1) : (K > 1 ? K : 1),
                       nullptr, transB ? (K > 1 ? K : 1) : (N > 1 ? N : 1), nullptr, N > 1 ? N : 1,
@@ -492,9 +523,9 @@ size_t dg_gemm_splitk_workspace_size(int64_t M, int64_t N, int splits)
     return (size_t)splits * (size_t)M * (size_t)N * 4;
 }
 
-int dg_select_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+int dg_select_kernel(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, const void *A,
                      int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
-                     int dtype)
+                     dg_dtype_t dtype)
 {
     int rc = validate(transA, transB, M, N, K, 1.f, A, lda, B, ldb, C, ldc, dtype, false);
     if (rc) return rc;

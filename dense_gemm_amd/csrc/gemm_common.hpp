@@ -26,7 +26,9 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 
 // Everything a kernel needs for one act(alpha*op(A)*op(B) + beta*C + bias),
-// or a strided batch of them.
+// or a strided batch of them.  A and B hold the operand type; C and the bias
+// hold the output type (the operand type, or fp32 for 16-bit operands with
+// an fp32 output).
 struct GemmParams {
     const void *A;
     const void *B;
@@ -57,13 +59,13 @@ struct GemmParams {
 typedef hipError_t (*launch_fn)(const GemmParams &p, hipStream_t stream);
 
 #ifdef __HIPCC__
-// Point A, B and C at batch b.
-template <typename T>
+// Point A, B (elements of type T) and C (elements of type TC) at batch b.
+template <typename T, typename TC = T>
 __device__ __forceinline__ void select_batch(GemmParams &p, int b)
 {
     p.A = (const T *)p.A + (int64_t)b * p.strideA;
     p.B = (const T *)p.B + (int64_t)b * p.strideB;
-    p.C = (T *)p.C + (int64_t)b * p.strideC;
+    p.C = (TC *)p.C + (int64_t)b * p.strideC;
 }
 
 // gelu(x) = x * Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2, in fp32.  erf by

@@ -31,12 +31,19 @@ const launch_fn *f32_launchers(int config)
 //   1: 256x256 tile, 4 stages, 8 waves of 128x64 (one workgroup per CU)
 //   2: 128x128 tile, 4 stages, 4 waves of 64x64 (two workgroups per CU)
 //   3, 4: configs 0 and 2 with 4-byte direct loads (rows not 16-byte aligned)
+//   5: 128x64 tile, 4 stages, 4 waves of 64x32 (grids too small for the
+//      128x128 tile to give every compute unit one: tall-skinny outputs)
+//   6: 64x64 tile, 4 stages, 4 waves of 32x32 (two or more workgroups per CU)
+//   7, 8: configs 5 and 6 with 4-byte direct loads
+#define DG_PIPE4(BM, BN, WM, WN, ST)                                                                \
+    {launch_pipe<float, BM, BN, WM, WN, false, false, ST, 1>, launch_pipe<float, BM, BN, WM, WN, false, true, ST, 1>, \
+     launch_pipe<float, BM, BN, WM, WN, true, false, ST, 1>, launch_pipe<float, BM, BN, WM, WN, true, true, ST, 1>}
 #define DG_PIPE4DW(BM, BN, WM, WN, ST)                                                              \
     {launch_pipe<float, BM, BN, WM, WN, false, false, ST, 1, 4>, launch_pipe<float, BM, BN, WM, WN, false, true, ST, 1, 4>, \
      launch_pipe<float, BM, BN, WM, WN, true, false, ST, 1, 4>, launch_pipe<float, BM, BN, WM, WN, true, true, ST, 1, 4>}
 const launch_fn *f32_pipe_launchers(int config)
 {
-    static const launch_fn table[5][4] = {
+    static const launch_fn table[9][4] = {
         {launch_pipe<float, 256, 128, 128, 64, false, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, false, true, 3, 1>,
          launch_pipe<float, 256, 128, 128, 64, true, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, true, true, 3, 1>},
         {launch_pipe<float, 256, 256, 128, 64, false, false, 4, 1>, launch_pipe<float, 256, 256, 128, 64, false, true, 4, 1>,
@@ -45,9 +52,14 @@ const launch_fn *f32_pipe_launchers(int config)
          launch_pipe<float, 128, 128, 64, 64, true, false, 4, 1>, launch_pipe<float, 128, 128, 64, 64, true, true, 4, 1>},
         DG_PIPE4DW(256, 128, 128, 64, 3),
         DG_PIPE4DW(128, 128, 64, 64, 4),
+        DG_PIPE4(128, 64, 64, 32, 4),
+        DG_PIPE4(64, 64, 32, 32, 4),
+        DG_PIPE4DW(128, 64, 64, 32, 4),
+        DG_PIPE4DW(64, 64, 32, 32, 4),
     };
     return table[config];
 }
+#undef DG_PIPE4
 #undef DG_PIPE4DW
 
 }  // namespace dg

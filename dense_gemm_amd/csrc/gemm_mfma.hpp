@@ -176,7 +176,8 @@ struct Operand {
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VEC, int MINW>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VEC, int MINW,
+          typename TC = T>
 __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
 {
     constexpr bool F16 = sizeof(T) == 2;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
     constexpr int STAGE = OpA::ELEMS + OpB::ELEMS;
     __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
 
-    select_batch<T>(p, blockIdx.y);
+    select_batch<T, TC>(p, blockIdx.y);
     int bid, split, k_begin, Kl;
     split_of(p, bid, split, k_begin, Kl);
     // this split's k range starts at k_begin: offset the operands to it
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
     // Epilogue.  Accumulator register r of lane l in a 32x32 block holds
     // row 8*(r/4) + 4*(l/32) + r%4, column l%32: for a fixed r the 32 lanes
     // of a half-wave hold 32 consecutive columns of one row.
-    T *C = (T *)p.C;
+    TC *C = (TC *)p.C;
     const int lcol = lane & 31;
     const int lrow4 = (lane >> 5) * 4;
 #pragma unroll
@@ -314,22 +315,23 @@ __global__ __launch_bounds__(256, MINW) void gemm_mfma_kernel(GemmParams p)
                 if (row < p.M && p.splits > 1) {
                     p.ws[((int64_t)split * p.M + row) * p.N + col] = acc[i][j][r];
                 } else if (row < p.M) {
-                    T *c = C + (int64_t)row * p.ldc + col;
+                    TC *c = C + (int64_t)row * p.ldc + col;
                     const float cin = p.beta != 0.f ? (float)*c : 0.f;
-                    *c = (T)epilogue_value<T>(p, acc[i][j][r], cin, col);
+                    *c = (TC)epilogue_value<TC>(p, acc[i][j][r], cin, col);
                 }
             }
         }
     }
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VEC, int MINW>
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool TA, bool TB, bool VEC, int MINW,
+          typename TC = T>
 hipError_t launch_mfma(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_mfma_kernel<T, BM, BN, BK, WM, WN, TA, TB, VEC, MINW>,
+    return hipLaunchKernel((const void *)&gemm_mfma_kernel<T, BM, BN, BK, WM, WN, TA, TB, VEC, MINW, TC>,
                            dim3(nwg, p.batch), dim3(256), args, 0, s);
 }
 

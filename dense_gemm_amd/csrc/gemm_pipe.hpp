@@ -464,9 +464,10 @@ struct PipeOperandS {
 // same sub-tile in the other group).  A 256 x 128 tile gets its two waves per
 // SIMD from eight 64 x 64 sub-tiles instead (KSPLIT = 1).
 // LB: bytes per lane of each direct load, 16, or 4 for rows that are not
-// 16-byte aligned.
+// 16-byte aligned.  TC: the element type of C and the bias (T, or fp32 for an
+// fp32 output of 16-bit operands).
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
-          int LB = 16>
+          int LB = 16, typename TC = T>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_pipe_kernel(GemmParams p)
 {
     constexpr bool HALF = sizeof(T) == 2;          // fp16 or bf16 operands
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     const int wm0 = (wq / WAVES_N) * WM;
     const int wn0 = (wq % WAVES_N) * WN;
     const int kk0 = kgroup * KPW;
-    select_batch<T>(p, blockIdx.y);
+    select_batch<T, TC>(p, blockIdx.y);
     int bid, split, k_begin, Kl;
     split_of(p, bid, split, k_begin, Kl);
     int tm, tn;
@@ -848,8 +849,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     // or when C rows are not 16-byte aligned.  The 16-byte stores of a 16-bit
     // C carry the non-temporal hint (C is not read again by the kernel); fp32
     // C and the 256x128 tile keep plain stores, which measured faster there.
-    constexpr bool NT_STORE = HALF && !(BM == 256 && BN == 128);
-    T *C = (T *)p.C;
+    constexpr bool HALF_C = sizeof(TC) == 2;       // 16-bit output
+    constexpr bool NT_STORE = HALF_C && !(BM == 256 && BN == 128);
+    typedef TC VC8 __attribute__((ext_vector_type(8)));
+    TC *C = (TC *)p.C;
     lds_char_t *stg = smem + wave * 32 * EPI_LD * 4;
     typedef __attribute__((address_space(3))) float lds_float_t;
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
@@ -892,14 +895,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             continue;
         }
         // alpha, beta, bias and the activation in fp32, one rounding to T
-        T *c = C + (int64_t)grow * p.ldc + gcol;
+        TC *c = C + (int64_t)grow * p.ldc + gcol;
         if (p.c_vec && grow < p.M && gcol + 16 <= p.N) {
             float cin[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) cin[e] = 0.f;
             if (p.beta != 0.f) {
-                if constexpr (HALF) {
-                    const V8 c0 = *(const V8 *)c, c1 = *(const V8 *)(c + 8);
+                if constexpr (HALF_C) {
+                    const VC8 c0 = *(const VC8 *)c, c1 = *(const VC8 *)(c + 8);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         cin[e] = (float)c0[e];
@@ -914,20 +917,20 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                     }
                 }
             }
-            epilogue_row16<T>(p, v, cin, gcol);
-            if constexpr (HALF) {
-                V8 o0, o1;
+            epilogue_row16<TC>(p, v, cin, gcol);
+            if constexpr (HALF_C) {
+                VC8 o0, o1;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    o0[e] = (T)v[e];
-                    o1[e] = (T)v[8 + e];
+                    o0[e] = (TC)v[e];
+                    o1[e] = (TC)v[8 + e];
                 }
                 if constexpr (NT_STORE) {
-                    __builtin_nontemporal_store(o0, (V8 *)c);
-                    __builtin_nontemporal_store(o1, (V8 *)(c + 8));
+                    __builtin_nontemporal_store(o0, (VC8 *)c);
+                    __builtin_nontemporal_store(o1, (VC8 *)(c + 8));
                 } else {
-                    *(V8 *)c = o0;
-                    *(V8 *)(c + 8) = o1;
+                    *(VC8 *)c = o0;
+                    *(VC8 *)(c + 8) = o1;
                 }
             } else {
 #pragma unroll
@@ -939,7 +942,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             for (int e = 0; e < 16; ++e) {
                 if (gcol + e < p.N) {
                     const float cin = p.beta != 0.f ? (float)c[e] : 0.f;
-                    c[e] = (T)epilogue_value<T>(p, v[e], cin, gcol + e);
+                    c[e] = (TC)epilogue_value<TC>(p, v[e], cin, gcol + e);
                 }
             }
         }
@@ -947,13 +950,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
-          int LB = 16>
+          int LB = 16, typename TC = T>
 hipError_t launch_pipe(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT, LB>,
+    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT, LB, TC>,
                            dim3(nwg, p.batch), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
 }
 

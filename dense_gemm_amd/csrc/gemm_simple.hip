@@ -1,6 +1,7 @@
 // Generic GEMM kernel: any shape, any leading dimension, any alignment, all
-// four transpose pairs, fp32, fp16 or bf16 operands, fp32 accumulation, the
-// bias + activation epilogue and strided batches (grid z).
+// four transpose pairs, fp32, fp16 or bf16 operands, fp32 accumulation, an
+// output of the operand type or fp32, the bias + activation epilogue and
+// strided batches (grid z).
 //
 // Structure: the shared-memory tiling of "Optimizing GEMM on Apple's M5 from
 // scratch, Part 1" (Kernels 2 and 3: stage a tile of each operand on chip,
@@ -27,15 +28,15 @@ constexpr int SPAD = 4;
 template <typename T>
 __device__ __forceinline__ float to_f32(T v) { return (float)v; }
 
-template <typename T, bool TA, bool TB>
+template <typename T, bool TA, bool TB, typename TC>
 __global__ __launch_bounds__(256) void gemm_simple_kernel(GemmParams p)
 {
     __shared__ float As[SK][ST + SPAD];
     __shared__ float Bs[SK][ST + SPAD];
-    select_batch<T>(p, blockIdx.z);
+    select_batch<T, TC>(p, blockIdx.z);
     const T *A = (const T *)p.A;
     const T *B = (const T *)p.B;
-    T *C = (T *)p.C;
+    TC *C = (TC *)p.C;
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     const int m0 = blockIdx.y * ST, n0 = blockIdx.x * ST;
@@ -96,9 +97,9 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(GemmParams p)
         for (int j = 0; j < 4; ++j) {
             const int gn = n0 + tx * 4 + j;
             if (gn >= p.N) continue;
-            T *c = C + (int64_t)gm * p.ldc + gn;
+            TC *c = C + (int64_t)gm * p.ldc + gn;
             const float cin = p.beta != 0.f ? to_f32(*c) : 0.f;
-            *c = (T)epilogue_value<T>(p, acc[i][j], cin, gn);
+            *c = (TC)epilogue_value<TC>(p, acc[i][j], cin, gn);
         }
     }
 }
@@ -150,13 +151,13 @@ hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t s)
                            args, 0, s);
 }
 
-template <typename T, bool TA, bool TB>
+template <typename T, bool TA, bool TB, typename TC = T>
 hipError_t launch_simple(const GemmParams &p, hipStream_t s)
 {
     dim3 grid((p.N + ST - 1) / ST, (p.M + ST - 1) / ST, p.batch);
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_simple_kernel<T, TA, TB>, grid, dim3(256), args, 0, s);
+    return hipLaunchKernel((const void *)&gemm_simple_kernel<T, TA, TB, TC>, grid, dim3(256), args, 0, s);
 }
 
 template <typename T>
@@ -173,30 +174,36 @@ hipError_t launch_scale(const GemmParams &p, hipStream_t s)
 
 }  // namespace
 
-// launchers exported to the dispatcher: [dtype][transA][transB]
+// launchers exported to the dispatcher, indexed by the dtype of the C ABI:
+// 0 fp32; 1 fp16 -> fp16; 2 bf16 -> bf16; 3 fp16 -> fp32; 4 bf16 -> fp32.
+// [dtype][transA][transB]
 launch_fn simple_launcher(int dtype, int ta, int tb)
 {
-    static const launch_fn table[3][2][2] = {
-        {{launch_simple<float, false, false>, launch_simple<float, false, true>},
-         {launch_simple<float, true, false>, launch_simple<float, true, true>}},
-        {{launch_simple<_Float16, false, false>, launch_simple<_Float16, false, true>},
-         {launch_simple<_Float16, true, false>, launch_simple<_Float16, true, true>}},
-        {{launch_simple<__bf16, false, false>, launch_simple<__bf16, false, true>},
-         {launch_simple<__bf16, true, false>, launch_simple<__bf16, true, true>}},
+#define DG_SIMPLE4(T, TC)                                                                          \
+    {{launch_simple<T, false, false, TC>, launch_simple<T, false, true, TC>},                      \
+     {launch_simple<T, true, false, TC>, launch_simple<T, true, true, TC>}}
+    static const launch_fn table[5][2][2] = {
+        DG_SIMPLE4(float, float), DG_SIMPLE4(_Float16, _Float16), DG_SIMPLE4(__bf16, __bf16),
+        DG_SIMPLE4(_Float16, float), DG_SIMPLE4(__bf16, float),
     };
+#undef DG_SIMPLE4
     return table[dtype][ta][tb];
 }
 
+// The reduction and the scale kernel touch only C (and the bias): they go by
+// the output type.
 launch_fn splitk_reduce_launcher(int dtype)
 {
-    static const launch_fn table[3] = {launch_splitk_reduce<float>, launch_splitk_reduce<_Float16>,
-                                       launch_splitk_reduce<__bf16>};
+    static const launch_fn table[5] = {launch_splitk_reduce<float>, launch_splitk_reduce<_Float16>,
+                                       launch_splitk_reduce<__bf16>, launch_splitk_reduce<float>,
+                                       launch_splitk_reduce<float>};
     return table[dtype];
 }
 
 launch_fn scale_launcher(int dtype)
 {
-    static const launch_fn table[3] = {launch_scale<float>, launch_scale<_Float16>, launch_scale<__bf16>};
+    static const launch_fn table[5] = {launch_scale<float>, launch_scale<_Float16>, launch_scale<__bf16>,
+                                       launch_scale<float>, launch_scale<float>};
     return table[dtype];
 }
 

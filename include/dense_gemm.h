@@ -38,7 +38,16 @@
  *                  round-to-nearest-even to bf16 at the end.  The page above
  *                  (section 1) has bf16 emulated on its GPU; gfx950 has a
  *                  native bf16 matrix-core instruction.
- *   alpha and beta are fp32 for every type.
+ *   DG_F16_F32OUT  A, B are fp16, C is fp32: the fp16 matrix-core path with
+ *                  fp32 accumulators, and alpha*acc + beta*C (fp32 C read as
+ *                  is) written to C in fp32 with no rounding to fp16 -- the
+ *                  fp32-output variant of "Metal GEMM Kernels for LoRA
+ *                  Training", section 4 (writing fp32 straight to device
+ *                  memory), for callers that keep fp32 results (gradient
+ *                  accumulation, a following fp32 reduction).
+ *   DG_BF16_F32OUT A, B are bf16, C is fp32; as DG_F16_F32OUT otherwise.
+ *   alpha and beta are fp32 for every type.  The bias of dg_gemm_ex has C's
+ *   type.
  *
  * Special values of the arguments:
  *   M == 0 or N == 0       nothing is done (returns DG_OK).
@@ -75,10 +84,28 @@
 extern "C" {
 #endif
 
-enum { DG_OP_N = 0, DG_OP_T = 1 };
-enum { DG_F32 = 0, DG_F16_F32ACC = 1, DG_BF16_F32ACC = 2 };
+/* The enumerations are int-sized in both languages (C++ fixes the underlying
+ * type, so that every int a caller passes is a value of the parameter's type
+ * and the library's own range checks see it); the ABI passes them as int. */
+#ifdef __cplusplus
+#define DG_ENUM(name) enum name : int
+#else
+#define DG_ENUM(name) enum name
+#endif
+
+/* op(X): X as stored (N) or its transpose (T). */
+typedef DG_ENUM(dg_op) { DG_OP_N = 0, DG_OP_T = 1 } dg_op_t;
+/* Operand, accumulator and output types (see "Types" above). */
+typedef DG_ENUM(dg_dtype) {
+    DG_F32 = 0,          /* A, B, C fp32; fp32 accumulation            */
+    DG_F16_F32ACC = 1,   /* A, B, C fp16; fp32 accumulation, fp16 out  */
+    DG_BF16_F32ACC = 2,  /* A, B, C bf16; fp32 accumulation, bf16 out  */
+    DG_F16_F32OUT = 3,   /* A, B fp16; fp32 accumulation, C fp32       */
+    DG_BF16_F32OUT = 4   /* A, B bf16; fp32 accumulation, C fp32       */
+} dg_dtype_t;
 /* Epilogue activations of dg_gemm_ex. */
-enum { DG_EPI_NONE = 0, DG_EPI_RELU = 1, DG_EPI_GELU = 2 };
+typedef DG_ENUM(dg_epilogue) { DG_EPI_NONE = 0, DG_EPI_RELU = 1, DG_EPI_GELU = 2 } dg_epilogue_t;
+#undef DG_ENUM
 
 #define DG_OK 0
 #define DG_ERR_UNSUPPORTED (-100)
@@ -88,9 +115,9 @@ enum { DG_EPI_NONE = 0, DG_EPI_RELU = 1, DG_EPI_GELU = 2 };
 #define DG_KERNEL_AUTO (-1)
 
 /* C = alpha * op(A) * op(B) + beta * C  (see above). */
-int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
-            int64_t lda, const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype,
-            void *stream);
+int dg_gemm(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha,
+            const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
+            int64_t ldc, dg_dtype_t dtype, void *stream);
 
 /* Same as dg_gemm, but runs kernel `kernel` (an index into the library's
  * kernel table, see dg_kernel_count / dg_kernel_name) instead of the one the
@@ -100,9 +127,9 @@ int dg_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha
  * kernels address a tile's operands with 32-bit byte offsets, so they need
  * 256 rows of the stored A and of the stored B to span less than 2^31
  * bytes).  For tests and measurement. */
-int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
-                        const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
-                        void *C, int64_t ldc, int dtype, void *stream, int kernel);
+int dg_gemm_with_kernel(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K,
+                        float alpha, const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
+                        void *C, int64_t ldc, dg_dtype_t dtype, void *stream, int kernel);
 
 /* Extended form: a fused bias + activation epilogue and strided batches.
  *
@@ -138,17 +165,18 @@ int dg_gemm_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K,
  * Special values as dg_gemm; with K == 0 or alpha == 0 the result is
  * act(beta*C + bias) and A and B are not read.  Pointer rules, asynchrony and
  * errors as dg_gemm (nothing enqueued on error).  No allocation. */
-int dg_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+int dg_gemm_ex(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha,
                const void *A, int64_t lda, int64_t strideA, const void *B, int64_t ldb,
                int64_t strideB, float beta, void *C, int64_t ldc, int64_t strideC,
-               int64_t batch, const void *bias, int epilogue, int dtype, void *stream);
+               int64_t batch, const void *bias, dg_epilogue_t epilogue, dg_dtype_t dtype,
+               void *stream);
 
 /* dg_gemm_ex with a forced kernel, as dg_gemm_with_kernel (argument 22). */
-int dg_gemm_ex_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
-                           const void *A, int64_t lda, int64_t strideA, const void *B,
+int dg_gemm_ex_with_kernel(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K,
+                           float alpha, const void *A, int64_t lda, int64_t strideA, const void *B,
                            int64_t ldb, int64_t strideB, float beta, void *C, int64_t ldc,
-                           int64_t strideC, int64_t batch, const void *bias, int epilogue,
-                           int dtype, void *stream, int kernel);
+                           int64_t strideC, int64_t batch, const void *bias,
+                           dg_epilogue_t epilogue, dg_dtype_t dtype, void *stream, int kernel);
 
 /* Split-K form of dg_gemm, for outputs too small to give every compute unit a
  * tile (skinny and low-rank products): K is cut into `splits` ranges (each a
@@ -170,15 +198,16 @@ int dg_gemm_ex_with_kernel(int transA, int transB, int64_t M, int64_t N, int64_t
  *               ranges actually used: -18.  Two calls that share a workspace
  *               must be ordered on one stream.
  * Otherwise as dg_gemm (arguments 1-15, same errors, asynchronous). */
-int dg_gemm_splitk(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+int dg_gemm_splitk(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, float alpha,
                    const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
-                   int64_t ldc, int dtype, void *stream, int splits, void *workspace,
+                   int64_t ldc, dg_dtype_t dtype, void *stream, int splits, void *workspace,
                    size_t workspace_bytes);
 
 /* The number of K ranges dg_gemm_splitk uses when called with splits = 0
  * (1 when splitting does not pay), or a negative status for invalid
  * arguments (host logic only). */
-int dg_gemm_splitk_choose(int transA, int transB, int64_t M, int64_t N, int64_t K, int dtype);
+int dg_gemm_splitk_choose(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K,
+                          dg_dtype_t dtype);
 
 /* Bytes of workspace dg_gemm_splitk needs for `splits` K ranges (0 when
  * splits <= 1 or the output is empty). */
@@ -186,9 +215,9 @@ size_t dg_gemm_splitk_workspace_size(int64_t M, int64_t N, int splits);
 
 /* The kernel dg_gemm would run for these arguments (host logic only, no GPU
  * call), or a negative status as dg_gemm would return it. */
-int dg_select_kernel(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+int dg_select_kernel(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K, const void *A,
                      int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
-                     int dtype);
+                     dg_dtype_t dtype);
 
 /* Number of kernels in the table, and a static name for kernel i (NULL when
  * i is out of range).  Names read "<dtype>_<tiles>_<variant>". */

@@ -140,9 +140,17 @@ def store(logical: np.ndarray, trans: bool, ld: int | None = None, pad_value=np.
 # Workload recipes (shapes, distributions and seeds of the measured problems)
 # ---------------------------------------------------------------------------
 
+# Storage types of the operands and of C for each dtype name: the operand type
+# itself, or (names ending in "o32") 16-bit operands with an fp32 C.
+OPERAND_TYPE = {"f32": "f32", "f16": "f16", "bf16": "bf16", "f16o32": "f16", "bf16o32": "bf16"}
+OUTPUT_TYPE = {"f32": "f32", "f16": "f16", "bf16": "bf16", "f16o32": "f32", "bf16o32": "f32"}
+
+
 def problem(M: int, N: int, K: int, dtype: str, dist: str, seed: int, with_c0: bool = False,
             std: float = 1.0):
-    """Logical op(A) [M,K], op(B) [K,N] and optional C0 [M,N], rounded to `dtype`.
+    """Logical op(A) [M,K], op(B) [K,N] rounded to the operand type of
+    `dtype`, and optional C0 [M,N] rounded to its output type (the draws are
+    the same for every dtype name, so "f16" and "f16o32" share operands).
 
     dist: "uniform" (iid uniform[-1,1)), "normal_sqrtk" (iid N(0,1)/sqrt(K)),
           "normal" (iid N(0, std^2)), "int2" (integers in [-2, 2]).
@@ -160,9 +168,9 @@ def problem(M: int, N: int, K: int, dtype: str, dist: str, seed: int, with_c0: b
             return st.integers(shape, -2, 2)
         raise ValueError(dist)
 
-    a = round_to(draw((M, K)), dtype)
-    b = round_to(draw((K, N)), dtype)
-    c0 = round_to(draw((M, N)), dtype) if with_c0 else None
+    a = round_to(draw((M, K)), OPERAND_TYPE[dtype])
+    b = round_to(draw((K, N)), OPERAND_TYPE[dtype])
+    c0 = round_to(draw((M, N)), OUTPUT_TYPE[dtype]) if with_c0 else None
     return a, b, c0
 
 
@@ -195,8 +203,10 @@ LORA_GEMMS = [
 ]
 
 
-def lora_problem(index: int, seed: int = 3):
-    """Logical fp16 operands of one LoRA-step GEMM (and C0 when beta != 0).
+def lora_problem(index: int, seed: int = 3, out: str = "f16"):
+    """Logical fp16 operands of one LoRA-step GEMM (and C0 when beta != 0,
+    rounded to `out`, the type of C: "f16", or "f32" for the fp32-output
+    form of the step).
 
     Each GEMM draws from its own stream (seed, then the GEMM's index in the
     list mixed into the seed), weights iid N(0, 0.02), activations and
@@ -207,5 +217,5 @@ def lora_problem(index: int, seed: int = 3):
     std = {"w": 0.02, "a": 1.0}
     a = round_to(st.normal((M, K), std[kinds[0]]), "f16")
     b = round_to(st.normal((K, N), std[kinds[1]]), "f16")
-    c0 = round_to(st.normal((M, N), 1.0), "f16") if beta != 0.0 else None
+    c0 = round_to(st.normal((M, N), 1.0), out) if beta != 0.0 else None
     return a, b, c0

@@ -8,7 +8,10 @@ import numpy as np
 import oracle
 import synth
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "f16o32": 3, "bf16o32": 4}
+# storage types of the operands and of C per dtype name
+OPND = synth.OPERAND_TYPE
+OUTT = synth.OUTPUT_TYPE
 EPI = {"none": 0, "relu": 1, "gelu": 2}
 
 
@@ -53,10 +56,10 @@ class Problem:
         self.ldc = N + pad[2]
         if c0 is not None:
             cinit = c0
-        elif dtype == "bf16":
+        elif OUTT[dtype] == "bf16":
             cinit = np.full((M, N), synth.BF16_NAN, dtype=np.uint16)
         else:
-            cinit = np.full((M, N), np.nan, dtype=a.dtype)
+            cinit = np.full((M, N), np.nan, dtype=np.float32 if OUTT[dtype] == "f32" else a.dtype)
         self.C0, _ = synth.store(cinit, False, self.ldc)
 
     @property
@@ -88,29 +91,30 @@ class Problem:
         import dense_gemm_amd as dg
         dev = torch.device("cuda:0")
 
-        def up(x, off):
-            flat = torch.empty(x.size + off + 8, dtype=torch_dtype(self.dtype), device=dev)
+        def up(x, off, st):
+            flat = torch.empty(x.size + off + 8, dtype=torch_dtype(st), device=dev)
             flat.fill_(float("nan"))
-            flat[off:off + x.size] = to_device(x, self.dtype, dev)
+            flat[off:off + x.size] = to_device(x, st, dev)
             return flat, off
 
-        At, oa = up(self.A, offset[0])
-        Bt, ob = up(self.B, offset[1])
-        Ct, oc = up(self.C0, offset[2])
+        At, oa = up(self.A, offset[0], OPND[self.dtype])
+        Bt, ob = up(self.B, offset[1], OPND[self.dtype])
+        Ct, oc = up(self.C0, offset[2], OUTT[self.dtype])
         es = At.element_size()
+        esc = Ct.element_size()
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         if self.extended:
-            bias_t = to_device(self.bias, self.dtype, dev) if self.bias is not None else None
+            bias_t = to_device(self.bias, OUTT[self.dtype], dev) if self.bias is not None else None
             rc = dg.dg_gemm_ex_with_kernel(
                 self.ta, self.tb, self.M, self.N, self.K, self.alpha, At.data_ptr() + oa * es,
                 self.lda, 0, Bt.data_ptr() + ob * es, self.ldb, 0, self.beta,
-                Ct.data_ptr() + oc * es, self.ldc, 0, 1,
+                Ct.data_ptr() + oc * esc, self.ldc, 0, 1,
                 bias_t.data_ptr() if bias_t is not None else None, EPI[self.act],
                 DTYPES[self.dtype], s.cuda_stream, kernel)
         else:
             rc = dg.dg_gemm_with_kernel(self.ta, self.tb, self.M, self.N, self.K, self.alpha,
                                         At.data_ptr() + oa * es, self.lda, Bt.data_ptr() + ob * es,
-                                        self.ldb, self.beta, Ct.data_ptr() + oc * es, self.ldc,
+                                        self.ldb, self.beta, Ct.data_ptr() + oc * esc, self.ldc,
                                         DTYPES[self.dtype], s.cuda_stream, kernel)
         if rc != 0:
             raise dg.GemmError(rc)
@@ -195,13 +199,13 @@ class Batched:
         self.sA = 0 if shared[0] else ar * ac + gap[0]
         self.sB = 0 if shared[1] else br * bc + gap[1]
         self.sC = M * N + gap[2]
-        nanv = synth.BF16_NAN if dtype == "bf16" else np.nan
-        dt = probs[0][0].dtype
+        def flat(stride, size, st, like):
+            nanv = synth.BF16_NAN if st == "bf16" else np.nan
+            return np.full(stride * (nb - 1) + size, nanv, dtype=like.dtype)
 
-        def flat(stride, size):
-            return np.full(stride * (nb - 1) + size, nanv, dtype=dt)
-
-        self.A, self.B, self.C0 = flat(self.sA, ar * ac), flat(self.sB, br * bc), flat(self.sC, M * N)
+        self.A = flat(self.sA, ar * ac, OPND[dtype], probs[0][0])
+        self.B = flat(self.sB, br * bc, OPND[dtype], probs[0][1])
+        self.C0 = flat(self.sC, M * N, OUTT[dtype], probs[0][2])
         for q, (a, b, c0) in enumerate(probs):
             self.A[q * self.sA:q * self.sA + ar * ac] = (a.T if ta else a).ravel()
             self.B[q * self.sB:q * self.sB + br * bc] = (b.T if tb else b).ravel()
@@ -214,8 +218,9 @@ class Batched:
 
         import dense_gemm_amd as dg
         dev = torch.device("cuda:0")
-        At, Bt, Ct = (to_device(x, self.dtype, dev) for x in (self.A, self.B, self.C0))
-        bias_t = to_device(self.bias, self.dtype, dev) if self.bias is not None else None
+        At, Bt = (to_device(x, OPND[self.dtype], dev) for x in (self.A, self.B))
+        Ct = to_device(self.C0, OUTT[self.dtype], dev)
+        bias_t = to_device(self.bias, OUTT[self.dtype], dev) if self.bias is not None else None
         s = torch.cuda.current_stream(dev)
         rc = dg.dg_gemm_ex_with_kernel(self.ta, self.tb, self.M, self.N, self.K, self.alpha,
                                        At.data_ptr(), self.lda, self.sA, Bt.data_ptr(), self.ldb,

@@ -58,7 +58,7 @@ def call(**kw):
     (dict(M=-1), -3), (dict(N=-5), -4), (dict(K=-1), -5), (dict(M=2 ** 31), -3),
     (dict(A=NULL), -7), (dict(lda=15), -8), (dict(ta=1, lda=15), -8),
     (dict(B=NULL), -9), (dict(ldb=15), -10), (dict(tb=1, ldb=15), -10),
-    (dict(C=NULL), -12), (dict(ldc=15), -13), (dict(dtype=3), -14), (dict(dtype=-1), -14),
+    (dict(C=NULL), -12), (dict(ldc=15), -13), (dict(dtype=5), -14), (dict(dtype=-1), -14),
     # the first invalid argument is the one reported
     (dict(ta=9, M=-1, dtype=5), -1), (dict(lda=1, ldc=1), -8),
 ])
@@ -108,8 +108,41 @@ def test_forced_kernel_out_of_range_is_unsupported():
     del a
 
 
+def test_fp32_output_types_choose_the_operand_types_kernels():
+    """A 16-bit-operand problem with an fp32 output runs the kernel the same
+    problem with a 16-bit output would run (the kernels take the output type
+    as a parameter); forcing a kernel of the other operand type is refused."""
+    for dt16, dt32 in ((dg.DG_F16_F32ACC, dg.DG_F16_F32OUT), (dg.DG_BF16_F32ACC, dg.DG_BF16_F32OUT)):
+        for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            for M, N, K in ((2048, 2048, 2048), (512, 32, 5632), (4096, 4096, 4096), (130, 66, 70)):
+                lda, ldb = (M if ta else K), (K if tb else N)
+                k16 = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N, dt16)
+                k32 = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N, dt32)
+                assert k16 == k32 >= 0
+                assert dg.dg_gemm_splitk_choose(ta, tb, M, N, K, dt16) == \
+                    dg.dg_gemm_splitk_choose(ta, tb, M, N, K, dt32)
+    f32k = dg.dg_select_kernel(0, 0, 64, 64, 64, 256, 64, 256, 64, 256, 64, dg.DG_F32)
+    rc = dg.dg_gemm_with_kernel(0, 0, 64, 64, 64, 1.0, 0x1000, 64, 0x2000, 64, 0.0, 0x3000, 64,
+                                dg.DG_F16_F32OUT, NULL, f32k)
+    assert rc == dg.DG_ERR_UNSUPPORTED
+
+
+def test_fp32_output_bias_alignment_is_c_elements():
+    """dg_gemm_ex's bias has C's type: 4-byte alignment for an fp32 output,
+    2-byte for a 16-bit one (checked before any GPU call)."""
+    def ex(dtype, bias):
+        return dg.dg_gemm_ex(0, 0, 16, 16, 16, 1.0, 0x1000, 16, 0, 0x2000, 16, 0, 0.0, 0x3000, 16, 0,
+                             1, bias, dg.DG_EPI_NONE, dtype, NULL)
+    assert ex(dg.DG_F16_F32OUT, 0x4002) == -18
+    assert ex(dg.DG_BF16_F32OUT, 0x4001) == -18
+    assert ex(dg.DG_F16_F32ACC, 0x4001) == -18
+    # a valid call with an empty batch returns before any GPU work
+    assert dg.dg_gemm_ex(0, 0, 16, 16, 16, 1.0, 0x1000, 16, 0, 0x2000, 16, 0, 0.0, 0x3000, 16, 0,
+                         0, 0x4004, dg.DG_EPI_NONE, dg.DG_F16_F32OUT, NULL) == 0
+
+
 def test_selection_picks_matrix_core_kernels_of_the_right_type():
-    for dtype, prefix in ((0, "f32_"), (1, "f16_"), (2, "bf16_")):
+    for dtype, prefix in ((0, "f32_"), (1, "f16_"), (2, "bf16_"), (3, "f16_"), (4, "bf16_")):
         for M, N, K in ((4096, 4096, 4096), (2048, 2048, 2048), (512, 32, 5632), (1, 1, 1),
                         (8192, 256, 8192), (4095, 4097, 1031)):
             k = dg.dg_select_kernel(0, 0, M, N, K, NULL, K, NULL, N, NULL, N, dtype)
@@ -273,7 +306,7 @@ def call_ex(**kw):
     (dict(batch=-1), -17), (dict(batch=65536), -17),
     (dict(bias=0x4001), -18),            # fp16 bias not aligned to its element
     (dict(epi=3), -19), (dict(epi=-1), -19),
-    (dict(dtype=3), -20),
+    (dict(dtype=5), -20),
     (dict(ta=9, sA=-1, epi=7), -1),      # the first invalid argument is the one reported
 ])
 def test_ex_invalid_arguments(kw, code):
