@@ -275,10 +275,18 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // eight-wave kernel does no better than 256x128 and is not chosen.
         const int64_t r256 = ceil_div(big, 256), r128 = ceil_div(small, 256);
         const bool wide = r256 * 194 < r128 * 100;
-        if (pipe) return wide ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
+        // At most one 128x128 tile per CU: the 64x64 tile (four times the
+        // workgroups, two resident per CU) fills the GPU instead.  Measured
+        // against 128x128: 8192x256x8192 291-295 against 510-521 us (all
+        // four transpose pairs), 512^3 15 against 40, 1024^3 28 against 73,
+        // 512^2x8192 176 against 515, 3072x1024x2048 106 against 139, 2048^3
+        // 134 against 139 (256 tiles, one round); the 128x64 tile lies
+        // between them (291-304 us at 8192x256x8192, 24 us at 512^3).
+        const bool fill = small <= 256;
+        if (pipe) return fill ? K_F32_PIPE_64 : wide ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
         // rows not 16-byte aligned: the same kernels with 4-byte direct loads
         if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x))
-            return wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
+            return fill ? K_F32_PIPE_64_DW : wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
     // 16-bit operands: the tile is picked by how many CUs its tiles fill
@@ -359,6 +367,24 @@ int splits_for(int64_t tiles, int64_t K)
     return (int)s;
 }
 
+// The K ranges a call runs with on kernel family f: `splits` (0: the
+// library's choice for f's tile count) turned into ranges whose length is a
+// multiple of 64 (every kernel's K slab divides it).  1 when the generic
+// kernel runs (it has no split mode) or the ranges collapse into one;
+// *k_chunk receives the range length (0 without a split).
+int resolve_splits(const Family &f, int64_t M, int64_t N, int64_t K, int splits, int32_t *k_chunk)
+{
+    *k_chunk = 0;
+    if (f.kind == SIMPLE || K == 0) return 1;
+    if (splits == 0) splits = splits_for(ceil_div(M, f.bm) * ceil_div(N, f.bn), K);
+    if (splits <= 1) return 1;
+    const int64_t chunk = ceil_div(ceil_div(K, splits), 64) * 64;
+    const int64_t n = ceil_div(K, chunk);
+    if (n <= 1) return 1;
+    *k_chunk = (int32_t)chunk;
+    return (int)n;
+}
+
 int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
         const void *B, int64_t ldb, float beta, void *C, int64_t ldc, int dtype, void *stream,
         int kernel, int splits = 1, void *ws = nullptr, size_t ws_bytes = 0, const Ext &x = Ext())
@@ -411,17 +437,10 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
             p.tiles_m = (int32_t)ceil_div(M, f.bm);
             p.tiles_n = (int32_t)ceil_div(N, f.bn);
             p.group_m = f.group_m;
-            if (splits == 0) splits = splits_for((int64_t)p.tiles_m * p.tiles_n, K);
-            if (splits > 1) {
-                // k_chunk: a multiple of 64 (every kernel's K slab divides it)
-                p.k_chunk = (int32_t)(ceil_div(ceil_div(K, splits), 64) * 64);
-                p.splits = (int32_t)ceil_div(K, p.k_chunk);
-                if (p.splits > 1) {
-                    if ((size_t)p.splits * (size_t)M * (size_t)N * 4 > ws_bytes) return -18;
-                    p.ws = (float *)ws;
-                } else {
-                    p.k_chunk = 0;
-                }
+            p.splits = resolve_splits(f, M, N, K, splits, &p.k_chunk);
+            if (p.splits > 1) {
+                if ((size_t)p.splits * (size_t)M * (size_t)N * 4 > ws_bytes) return -18;
+                p.ws = (float *)ws;
             }
             const int vi = (f.kind == PIPE || f.kind == PIPE_DW || vec_ok(A, lda, B, ldb, dtype, x)) ? 0 : 4;
             err = (out32 ? f.variants32 : f.variants)(f.config)[vi + ta * 2 + tb](p, s);

@@ -175,8 +175,9 @@ def test_underfilled_16bit_grids_take_64x64_tiles_unsplit():
     assert dg.dg_gemm_splitk_choose(0, 0, 512, 2048, 16384, 1) > 1
     # enough 128x128 tiles (176 for the LoRA gate projection): unchanged
     assert tile_of(512, 5632, 2048) == (128, 128)
-    # fp32 is not affected
-    assert tile_of(512, 2048, 5632, 0) != (64, 64)
+    # fp32 has its own rule (at most 256 tiles of 128x128: 64x64, whatever K)
+    assert tile_of(512, 2048, 5632, 0) == (64, 64)
+    assert tile_of(4096, 4096, 512, 0) != (64, 64)
 
 
 def test_16bit_large_grids_take_the_tile_that_fills_the_cus_in_one_wave():
@@ -208,8 +209,16 @@ def test_fp32_tile_by_rounds():
     for M, N, K, tile in ((4096, 4096, 4096, (256, 128)), (8192, 8192, 8192, (256, 128)),
                           (4096, 4224, 4096, (128, 128)), (4608, 4096, 4096, (128, 128)),
                           (3072, 4096, 4096, (128, 128)), (5120, 4096, 2048, (128, 128)),
-                          (2048, 2048, 2048, (128, 128))):
+                          (2304, 2048, 2048, (256, 128))):
         assert tile_of(M, N, K, 0) == tile, (M, N, K)
+    # at most one 128x128 tile per CU: the 64x64 tile, every transpose pair
+    # (the tall-skinny 8192x256x8192 of the full-form workload, 512^3, 2048^3)
+    for M, N, K in ((8192, 256, 8192), (512, 512, 512), (2048, 2048, 2048), (256, 8192, 8192),
+                    (3072, 1024, 2048)):
+        for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            lda, ldb = (M if ta else K) + 8, (K if tb else N) + 8
+            k = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 8, 0)
+            assert dg.dg_kernel_name(k) == "f32_64x64_pipe4_mfma32x32x2", (M, N, K, ta, tb)
     # the 4-byte-load kernels follow the same rule (K and N not multiples of 4)
     k = dg.dg_select_kernel(0, 0, 4095, 4097, 1031, 256, 1031, 256, 4097, 256, 4097, 0)
     assert dg.dg_kernel_name(k) == "f32_128x128_pipe4_dw_mfma32x32x2"
