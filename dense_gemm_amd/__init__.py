@@ -20,7 +20,8 @@ DG_OP_N, DG_OP_T = 0, 1
 DG_F32, DG_F16_F32ACC, DG_BF16_F32ACC, DG_F16_F32OUT, DG_BF16_F32OUT = 0, 1, 2, 3, 4
 DG_EPI_NONE, DG_EPI_RELU, DG_EPI_GELU = 0, 1, 2
 EPILOGUES = {"none": DG_EPI_NONE, "relu": DG_EPI_RELU, "gelu": DG_EPI_GELU}
-DG_OK, DG_ERR_UNSUPPORTED, DG_ERR_HIP = 0, -100, -200
+DG_OK, DG_ERR_UNSUPPORTED, DG_ERR_SCRATCH, DG_ERR_HIP = 0, -100, -101, -200
+DG_SCRATCH_BYTES = 16 * 1024 * 1024
 DG_KERNEL_AUTO = -1
 
 if not os.path.exists(LIB_PATH):
@@ -48,6 +49,8 @@ _lib.dg_gemm_ex_with_kernel.argtypes = _EX_ARGS + [_ci]
 _lib.dg_gemm_ex_with_kernel.restype = _ci
 _lib.dg_gemm_splitk.argtypes = _GEMM_ARGS + [_ci, _vp, ctypes.c_size_t]
 _lib.dg_gemm_splitk.restype = _ci
+_lib.dg_gemm_splitk_noalloc.argtypes = _GEMM_ARGS + [_ci]
+_lib.dg_gemm_splitk_noalloc.restype = _ci
 _lib.dg_gemm_splitk_choose.argtypes = [_ci, _ci, _i64, _i64, _i64, _ci]
 _lib.dg_gemm_splitk_choose.restype = _ci
 _lib.dg_gemm_splitk_workspace_size.argtypes = [_i64, _i64, _ci]
@@ -70,7 +73,7 @@ _lib.dg_version.argtypes = []
 _lib.dg_version.restype = _ci
 
 EXPORTED = ["dg_gemm", "dg_gemm_with_kernel", "dg_gemm_ex", "dg_gemm_ex_with_kernel", "dg_gemm_splitk",
-            "dg_gemm_splitk_choose",
+            "dg_gemm_splitk_noalloc", "dg_gemm_splitk_choose",
             "dg_gemm_splitk_workspace_size", "dg_select_kernel", "dg_kernel_count",
             "dg_kernel_name", "dg_kernel_tile_m", "dg_kernel_tile_n", "dg_status_string",
             "dg_last_hip_error", "dg_version"]
@@ -127,6 +130,12 @@ def dg_gemm_splitk(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                    splits, workspace, workspace_bytes) -> int:
     return _lib.dg_gemm_splitk(int(transA), int(transB), M, N, K, alpha, A, lda, B, ldb, beta, C,
                                ldc, int(dtype), stream, int(splits), workspace, int(workspace_bytes))
+
+
+def dg_gemm_splitk_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype,
+                           stream, splits) -> int:
+    return _lib.dg_gemm_splitk_noalloc(int(transA), int(transB), M, N, K, alpha, A, lda, B, ldb,
+                                       beta, C, ldc, int(dtype), stream, int(splits))
 
 
 def dg_gemm_splitk_choose(transA, transB, M, N, K, dtype) -> int:

@@ -6,7 +6,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gemm_common.hpp"
+
+// The split-K scratch of dg_gemm_splitk_noalloc (see scratch_for below).
+static __device__ __align__(256) float scratch[DG_SCRATCH_BYTES / 4];
 
 namespace dg {
 launch_fn simple_launcher(int dtype, int ta, int tb);
@@ -454,6 +459,53 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     return DG_OK;
 }
 
+// ---- scratch memory of dg_gemm_splitk_noalloc ---------------------------------
+// The split-K partials of the allocation-free entry point live in this
+// device array, one copy per GPU (each device that loads the library's code
+// object gets its own), held until the process ends.  Host code never uses
+// the array's name as an address: its device address is looked up once per
+// device with hipGetSymbolAddress and kept in g_scratch.
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` belongs to (the
+// current device for the NULL stream), looked up on first use with that
+// device current.  Returns 0 or DG_ERR_HIP.
+int scratch_for(void *stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return DG_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        g_last_hip_error = (int)hipErrorInvalidDevice;
+        return DG_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void *ptr = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return DG_ERR_HIP;
+        }
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -520,6 +572,33 @@ int dg_gemm_splitk(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t
                DG_KERNEL_AUTO, splits, workspace, workspace_bytes);
 }
 
+int dg_gemm_splitk_noalloc(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K,
+                           float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                           float beta, void *C, int64_t ldc, dg_dtype_t dtype, void *stream,
+                           int splits)
+{
+    int rc = validate(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
+    if (rc) return rc;
+    if (splits < 0 || splits > 4096) return -16;
+    if (M == 0 || N == 0) return DG_OK;
+    // the ranges dg_gemm_splitk would use; more partials than the scratch
+    // holds are refused before anything is enqueued
+    int used = 1;
+    if (K > 0 && alpha != 0.f) {
+        const int k = choose(transA, transB, M, N, K, A, lda, B, ldb, dtype);
+        int32_t chunk;
+        used = resolve_splits(kFamilies[k], M, N, K, splits, &chunk);
+    }
+    void *ws = nullptr;
+    if (used > 1) {
+        if ((size_t)used * (size_t)M * (size_t)N * 4 > (size_t)DG_SCRATCH_BYTES) return DG_ERR_SCRATCH;
+        rc = scratch_for(stream, &ws);
+        if (rc) return rc;
+    }
+    return run(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream,
+               DG_KERNEL_AUTO, used > 1 ? splits : 1, ws, (size_t)DG_SCRATCH_BYTES);
+}
+
 int dg_gemm_splitk_choose(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K,
                           dg_dtype_t dtype)
 {
@@ -573,6 +652,7 @@ const char *dg_status_string(int status)
     switch (status) {
     case DG_OK: return "ok";
     case DG_ERR_UNSUPPORTED: return "kernel does not support this problem";
+    case DG_ERR_SCRATCH: return "split-K partials larger than the library's scratch (DG_SCRATCH_BYTES)";
     case DG_ERR_HIP: return "HIP error (see dg_last_hip_error)";
     case -1: return "invalid argument 1 (transA)";
     case -2: return "invalid argument 2 (transB)";
@@ -602,6 +682,6 @@ const char *dg_status_string(int status)
 
 int dg_last_hip_error(void) { return g_last_hip_error; }
 
-int dg_version(void) { return 300; }
+int dg_version(void) { return 400; }
 
 }  // extern "C"

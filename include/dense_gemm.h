@@ -71,6 +71,8 @@
  *                      NULL pointer with a non-empty extent, unknown dtype.
  *                      Nothing is enqueued.
  *   DG_ERR_UNSUPPORTED the forced kernel cannot run this problem.
+ *   DG_ERR_SCRATCH     (dg_gemm_splitk_noalloc) more partials than the
+ *                      library's scratch holds.
  *   DG_ERR_HIP         a HIP call failed; dg_last_hip_error() returns its
  *                      hipError_t (per calling thread).
  */
@@ -109,6 +111,7 @@ typedef DG_ENUM(dg_epilogue) { DG_EPI_NONE = 0, DG_EPI_RELU = 1, DG_EPI_GELU = 2
 
 #define DG_OK 0
 #define DG_ERR_UNSUPPORTED (-100)
+#define DG_ERR_SCRATCH (-101)
 #define DG_ERR_HIP (-200)
 
 /* Kernel choice for dg_gemm_with_kernel: DG_KERNEL_AUTO lets the library pick. */
@@ -202,6 +205,36 @@ int dg_gemm_splitk(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t
                    const void *A, int64_t lda, const void *B, int64_t ldb, float beta, void *C,
                    int64_t ldc, dg_dtype_t dtype, void *stream, int splits, void *workspace,
                    size_t workspace_bytes);
+
+/* Bytes of the library's own split-K scratch on each GPU (see
+ * dg_gemm_splitk_noalloc). */
+#define DG_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/* dg_gemm_splitk without a workspace and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The fp32 partials go to a
+ * device array inside the library, DG_SCRATCH_BYTES (16 MiB) on each GPU,
+ * which the GPU holds from the library's load until the process ends.  The
+ * call uses the K ranges dg_gemm_splitk would use for the same `splits` (0:
+ * the library's choice; 1: no split, the scratch is not touched), computes
+ * the same result with the same kernels, and enqueues the same work.
+ *   Arguments 1-16: as dg_gemm_splitk's first 16 (same errors, -16 for
+ *   splits below 0 or above 4096).
+ *   DG_ERR_SCRATCH: the partials, splits * M * N * 4 bytes for the ranges
+ *   used, exceed DG_SCRATCH_BYTES; nothing is enqueued (call dg_gemm_splitk
+ *   with a workspace, or fewer splits).
+ *   DG_ERR_HIP: looking up the scratch's device address failed (first call
+ *   on a device only).
+ * Every call on one GPU shares that GPU's scratch, and a call leaves its
+ * partials there: calls that may overlap on one GPU (on different streams,
+ * or from several host threads without ordering) race on it and must be
+ * ordered by the caller, for example on one stream.  No memory is cleared:
+ * the GEMM kernel writes every partial before the reduction reads it.
+ * Asynchronous, like dg_gemm; calls no allocating routine. */
+int dg_gemm_splitk_noalloc(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64_t K,
+                           float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                           float beta, void *C, int64_t ldc, dg_dtype_t dtype, void *stream,
+                           int splits);
 
 /* The number of K ranges dg_gemm_splitk uses when called with splits = 0
  * (1 when splitting does not pay), or a negative status for invalid
