@@ -558,6 +558,8 @@ def main():
     ap.add_argument("--no-lora", action="store_true", help="skip the LoRA-step GEMM sequence")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the SGEMM 512^3 and ragged full-form legs")
+    ap.add_argument("--no-aux", action="store_true",
+                    help="skip the attention-heads and fused-epilogue legs")
     ap.add_argument("--no-check", action="store_true",
                     help="skip the oracle checks of the timed outputs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -715,11 +717,11 @@ def main():
         out["sgemm_ragged"] = sgemm_ragged(dev, stream, max(args.steps // 2, 10))
 
     # ---- attention per-head products (strided batch over heads) ----------------
-    if not args.no_f16:
+    if not args.no_f16 and not args.no_aux:
         out["attention_heads"] = attention_heads(dev, stream, max(args.steps, 50))
 
     # ---- fused epilogue on the MLP up-projection -----------------------------
-    if not args.no_f16:
+    if not args.no_f16 and not args.no_aux:
         out["epilogue"] = epilogue_cost(dev, stream, max(args.steps, 100))
 
     # ---- LoRA MLP-block step: the 18 fp16 GEMMs of one forward + backward -------
