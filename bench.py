@@ -520,6 +520,40 @@ def sgemm_ragged(dev, stream, reps):
     return {"alpha": alpha, "beta": beta, "ld_pad": 8, **out}
 
 
+def f16_k_sweep(dev, stream, reps):
+    """fp16 M = N = 2048 over K = 64 .. 8192 (nn, tn, nt; the library's
+    kernel, event-timed back to back): the launch's time splits into a part
+    independent of K (launch, prologue, K-group sum, C stores) and a cost per
+    64-deep K slab, read off as the slope between the two largest K."""
+    import torch
+
+    import dense_gemm_amd as dg
+    S = 2048
+    Ks = (64, 128, 256, 512, 1024, 2048, 4096, 8192)
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(5)
+    for name, ta, tb in (("nn", 0, 0), ("tn", 1, 0), ("nt", 0, 1)):
+        us = {}
+        for K in Ks:
+            A = (torch.randn((K, S) if ta else (S, K), device=dev, generator=g) / 8).half()
+            B = (torch.randn((S, K) if tb else (K, S), device=dev, generator=g) / 8).half()
+            C = torch.empty((S, S), device=dev, dtype=torch.float16)
+            lda, ldb = (S if ta else K), (K if tb else S)
+
+            def f(ta=ta, tb=tb, K=K, A=A, B=B, C=C, lda=lda, ldb=ldb):
+                rc = dg.dg_gemm(ta, tb, S, S, K, 1.0, A.data_ptr(), lda, B.data_ptr(), ldb, 0.0,
+                                C.data_ptr(), S, dg.DG_F16_F32ACC, stream.cuda_stream)
+                if rc != 0:
+                    raise dg.GemmError(rc)
+
+            warm(f, 20, 0.05)
+            us[K] = round(min(time_launches(f, stream, reps) for _ in range(3)) * 1e6, 2)
+        slab = (us[8192] - us[4096]) / ((8192 - 4096) // 64)
+        out[name] = {"us_by_k": us, "us_per_slab": round(slab, 4),
+                     "k_independent_us": round(us[2048] - slab * (2048 // 64), 2)}
+    return out
+
+
 def smi_clocks(index=0):
     """Clock state from `amd-smi metric --clock --json` (a child process): the
     median current shader clock over the XCDs, its range, whether it is
@@ -558,6 +592,9 @@ def main():
     ap.add_argument("--no-lora", action="store_true", help="skip the LoRA-step GEMM sequence")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the SGEMM 512^3 and ragged full-form legs")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="also time fp16 M=N=2048 over K = 64 .. 8192 (cost per K slab and "
+                         "the K-independent part)")
     ap.add_argument("--no-aux", action="store_true",
                     help="skip the attention-heads and fused-epilogue legs")
     ap.add_argument("--no-check", action="store_true",
@@ -710,6 +747,9 @@ def main():
     # ---- bf16 2048^3 nn / tn / nt (same recipe as fp16) ------------------------
     if not args.no_f16:
         out["bf16_2048"] = bf16_square(dev, stream, max(args.steps, 200), not args.no_check)
+
+    if args.k_sweep:
+        out["f16_k_sweep"] = f16_k_sweep(dev, stream, 100)
 
     # ---- SGEMM 512^3 and the ragged full-form workloads -------------------------
     if not args.no_extra:
