@@ -270,28 +270,42 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
     const int64_t small = ceil_div(M, 128) * ceil_div(N, 128) * nb;
     const bool pipe = pipe_ok(ta, tb, M, N, K, A, lda, B, ldb, dtype, x);
     if (dtype == DG_F32) {
-        // Rounds of tiles: a CU runs its share of the tiles about ceil(tiles /
-        // 256) tile-times long, whether one or two of them are resident, and a
-        // 256x128 tile takes 1.94 times as long as a 128x128 one (both two
-        // workgroups per CU; measured at 4096 x 4096-4608 x 4096, 3072 x 4096
-        // x 4096, 5120 x 4096 x 2048, 6144^2 x 2048: the 128x128 tile 17-40%
-        // faster wherever the 256x128 tiles end in a partly filled round, 3%
-        // slower at 4096^3, where they fill two rounds exactly).  The 256x256
-        // eight-wave kernel does no better than 256x128 and is not chosen.
-        const int64_t r256 = ceil_div(big, 256), r128 = ceil_div(small, 256);
-        const bool wide = r256 * 194 < r128 * 100;
-        // At most one 128x128 tile per CU: the 64x64 tile (four times the
-        // workgroups, two resident per CU) fills the GPU instead.  Measured
-        // against 128x128: 8192x256x8192 291-295 against 510-521 us (all
-        // four transpose pairs), 512^3 15 against 40, 1024^3 28 against 73,
-        // 512^2x8192 176 against 515, 3072x1024x2048 106 against 139, 2048^3
-        // 134 against 139 (256 tiles, one round); the 128x64 tile lies
-        // between them (291-304 us at 8192x256x8192, 24 us at 512^3).
-        const bool fill = small <= 256;
-        if (pipe) return fill ? K_F32_PIPE_64 : wide ? K_F32_PIPE_256x128 : K_F32_PIPE_128;
-        // rows not 16-byte aligned: the same kernels with 4-byte direct loads
-        if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x))
-            return fill ? K_F32_PIPE_64_DW : wide ? K_F32_PIPE_256x128_DW : K_F32_PIPE_128_DW;
+        // The tile by its cost in rounds: a CU runs its share of the tiles in
+        // about ceil(tiles / 256) tile-times, whether one or two of them are
+        // resident, and a tile's time relative to a 128x128 one is 1.933
+        // (256x128), 0.51 (128x64) and 0.2636 (64x64).  Measured at 4096^3,
+        // the model then matched the fastest tile at 6144^3, 3584^3, 2560^3,
+        // 4096x4224x4096, 3072x4096x4096, 5120x4096x2048, 6144^2x2048,
+        // 2304x2048x2048, 2048x3072x2048, 8192^2x2048, 4096^2x1024 and
+        // 1024x16384x4096 (within 2-3% of its prediction).  256x128 is
+        // considered only when its tiles fill whole rounds of two per CU: with
+        // a partly filled last round it ran 20-27% slower than predicted
+        // (6144^3, 5120x4096x2048).  Small tiles win where the larger ones end
+        // in a partly filled round: 4095x4097x1031 (the 4097th column adds a
+        // whole tile column) 302-345 us against 410-498 on 128x128, 3584^3
+        // 729 against 822 on 256x128.  At most one 128x128 tile per CU: the
+        // 64x64 tile (two or more workgroups per CU), measured 8192x256x8192
+        // 291-295 against 510-521 us on 128x128 (all four transpose pairs),
+        // 512^3 15 against 40, 1024^3 28 against 73, 512^2x8192 176 against
+        // 515, 3072x1024x2048 106 against 139, 2048^3 134 against 139.
+        const int64_t t12864 = ceil_div(M, 128) * ceil_div(N, 64) * nb;
+        const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64) * nb;
+        int pk;                                    // 0: 256x128, 1: 128x128, 2: 128x64, 3: 64x64
+        if (small <= 256) {
+            pk = 3;
+        } else {
+            const double cost[4] = {(big % 512 == 0) ? ceil_div(big, 256) * 1.933 : 1e30,
+                                    (double)ceil_div(small, 256),
+                                    ceil_div(t12864, 256) * 0.51, ceil_div(t64, 256) * 0.2636};
+            pk = 0;
+            for (int c = 1; c < 4; ++c)
+                if (cost[c] < cost[pk]) pk = c;
+        }
+        static const int pipe16[4] = {K_F32_PIPE_256x128, K_F32_PIPE_128, K_F32_PIPE_128x64, K_F32_PIPE_64};
+        static const int pipe4[4] = {K_F32_PIPE_256x128_DW, K_F32_PIPE_128_DW, K_F32_PIPE_128x64_DW, K_F32_PIPE_64_DW};
+        if (pipe) return pipe16[pk];
+        // rows not 16-byte aligned: the same tiles with 4-byte direct loads
+        if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return pipe4[pk];
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
     // 16-bit operands: the tile is picked by how many CUs its tiles fill

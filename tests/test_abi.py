@@ -204,12 +204,17 @@ def test_16bit_large_grids_take_the_tile_that_fills_the_cus_in_one_wave():
 
 
 def test_fp32_tile_by_rounds():
-    # 256x128 only where its tiles fill whole rounds of 256 CUs better than
-    # 128x128 tiles do (1.94 tile-times each): the headline 4096^3 and 8192^3
-    for M, N, K, tile in ((4096, 4096, 4096, (256, 128)), (8192, 8192, 8192, (256, 128)),
-                          (4096, 4224, 4096, (128, 128)), (4608, 4096, 4096, (128, 128)),
+    # the tile with the fewest tile-times per CU (ceil(tiles / 256) times a
+    # tile's time relative to 128x128: 1.933, 1, 0.51, 0.2636), 256x128 only
+    # where its tiles fill whole rounds of two per CU; each of these was the
+    # fastest of the four tiles when measured
+    for M, N, K, tile in ((4096, 4096, 4096, (256, 128)), (8192, 8192, 2048, (256, 128)),
+                          (2048, 8192, 4096, (256, 128)), (4096, 4096, 1024, (256, 128)),
+                          (1024, 16384, 4096, (256, 128)), (6144, 6144, 6144, (128, 128)),
                           (3072, 4096, 4096, (128, 128)), (5120, 4096, 2048, (128, 128)),
-                          (2304, 2048, 2048, (256, 128))):
+                          (6144, 6144, 2048, (128, 128)), (2048, 3072, 2048, (128, 64)),
+                          (4096, 4224, 4096, (64, 64)), (2560, 2560, 2560, (64, 64)),
+                          (3584, 3584, 3584, (64, 64)), (2304, 2048, 2048, (64, 64))):
         assert tile_of(M, N, K, 0) == tile, (M, N, K)
     # at most one 128x128 tile per CU: the 64x64 tile, every transpose pair
     # (the tall-skinny 8192x256x8192 of the full-form workload, 512^3, 2048^3)
@@ -219,9 +224,10 @@ def test_fp32_tile_by_rounds():
             lda, ldb = (M if ta else K) + 8, (K if tb else N) + 8
             k = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 8, 0)
             assert dg.dg_kernel_name(k) == "f32_64x64_pipe4_mfma32x32x2", (M, N, K, ta, tb)
-    # the 4-byte-load kernels follow the same rule (K and N not multiples of 4)
+    # the 4-byte-load kernels follow the same rule (K and N not multiples of 4):
+    # 4097 columns end in a partly filled round of the larger tiles
     k = dg.dg_select_kernel(0, 0, 4095, 4097, 1031, 256, 1031, 256, 4097, 256, 4097, 0)
-    assert dg.dg_kernel_name(k) == "f32_128x128_pipe4_dw_mfma32x32x2"
+    assert dg.dg_kernel_name(k) == "f32_64x64_pipe4_dw_mfma32x32x2"
     k = dg.dg_select_kernel(0, 0, 4096, 4096, 4095, 256, 4095, 256, 4096, 256, 4096, 0)
     assert dg.dg_kernel_name(k) == "f32_256x128_pipe3_dw_mfma32x32x2"
 
