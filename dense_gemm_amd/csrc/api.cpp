@@ -326,7 +326,19 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // does a tile's work at 15-30% less time per flop (measured 3072^3 to
         // 8192^3 and 2304-4096 x 4096 x 512-16384: faster in every case but
         // one tie at 6144^3 nt, where 2.25 waves round up against 4.5).
+        // Past one full round of 256x256 tiles, the tile by its cost in
+        // rounds: a full round of 256x256 tiles takes 3.125 times one of
+        // 128x128 tiles (4096^3, K from 1024 to 6144), and a partly filled
+        // last round about 0.6 of a full one for either tile.  A few tiles
+        // past a full round then favour 128x128: 4608x4096x4096 183-189 us
+        // against 196-201, 4096x4224x4096 179-186 against 197-202 (all three
+        // transpose pairs), while 5120^2x1024 (1.56 rounds), 6144^3 (2.25)
+        // and 7168^2x1024 (3.06) keep 256x256, 10-30% faster there.
         const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256) * nb;
+        if (t256 > 256) {
+            auto rounds = [](int64_t t) { return (double)(t / 256) + (t % 256 ? 0.6 : 0.0); };
+            if (rounds(small) < 3.125 * rounds(t256)) return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
+        }
         if (t256 > 128) return bf ? K_BF16_PIPE_256x256 : K_F16_PIPE_256x256;
         // 256x128 tiles on more than half the CUs: the 256x128 kernel, save
         // for tn (both operands through transposed LDS reads), where the

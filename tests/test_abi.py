@@ -189,6 +189,16 @@ def test_16bit_large_grids_take_the_tile_that_fills_the_cus_in_one_wave():
                 k = dg.dg_select_kernel(ta, tb, M, N, K, 256, M if ta else K, 256, K if tb else N, 256, N,
                                         dtype)
                 assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 256), (M, N, K, ta, tb)
+        # a few 256x256 tiles past one full round of the CUs: 128x128, whose
+        # last round is the smaller loss; more rounds keep 256x256
+        for M, N, K, tile in ((4608, 4096, 4096, (128, 128)), (4096, 4224, 4096, (128, 128)),
+                              (4096, 4104, 1032, (128, 128)), (5120, 4096, 2048, (256, 256)),
+                              (5120, 5120, 1024, (256, 256)), (7168, 7168, 1024, (256, 256)),
+                              (8192, 8192, 8192, (256, 256))):
+            for ta, tb in ((0, 0), (1, 0), (0, 1)):
+                k = dg.dg_select_kernel(ta, tb, M, N, K, 256, M if ta else K, 256, K if tb else N, 256, N,
+                                        dtype)
+                assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == tile, (M, N, K, ta, tb)
         # 129-256 tiles of 256x128: 256x128 except tn, which keeps 128x128
         for M, N, K in ((2048, 4096, 4096), (2560, 2560, 4096), (8192, 1024, 1024)):
             assert tile_of(M, N, K, dtype) == (256, 128), (M, N, K)
