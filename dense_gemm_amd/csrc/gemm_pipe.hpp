@@ -838,10 +838,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
         // 4096^3 1.0-4.0% faster (the 4-byte-load kernel 9.7-10.4%),
         // 8192x256x8192 7.6-12.5%, 512^3 8-13%, the 128x64 tile 3%, the
         // 128x128 tile 2.5-5.6% except nt, which was 0-24% slower
-        // (6144^2x2048, 3072x4096^2, 5120x4096x2048) and keeps the general loop.
+        // (6144^2x2048, 3072x4096^2, 5120x4096x2048) and keeps the general
+        // loop.  The 64x64 tile takes it on grids of at most 1024 workgroups
+        // (four per CU): above that it measured 3-22% slower at 2304x2048^2,
+        // 3000^3 and 3072^3 (4.5 to 9 workgroups per CU).
         int kt = 0;
         if constexpr (!(BM == 128 && BN == 128 && !TA && TB)) {
-            const int nfast = (krem == BK ? nk : nk - 1) - (STAGES - 1);
+            const bool fast = !(BM == 64 && BN == 64) || gridDim.x * gridDim.y <= 1024;
+            const int nfast = fast ? (krem == BK ? nk : nk - 1) - (STAGES - 1) : 0;
             for (; kt < nfast; ++kt) fstep(std::true_type(), kt);
         }
         for (; kt < nk; ++kt) fstep(std::false_type(), kt);
