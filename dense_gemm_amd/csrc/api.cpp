@@ -69,14 +69,14 @@ const Family kFamilies[] = {
     {"f16_128x128_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, MFMA, dg::f16_launchers, 0, dg::f16_o32_launchers},
     {"f16_256x128_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, MFMA, dg::f16_launchers, 1, dg::f16_o32_launchers},
     {"f16_128x128_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 0, dg::f16_o32_pipe_launchers},
-    {"f16_256x128_pipe3_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1, dg::f16_o32_pipe_launchers},
+    {"f16_256x128_pipe2_w8_mfma32x32x16", DG_F16_F32ACC, 256, 128, 4, PIPE, dg::f16_pipe_launchers, 1, dg::f16_o32_pipe_launchers},
     {"f16_128x128_pipe2_ksplit2_mfma32x32x16", DG_F16_F32ACC, 128, 128, 4, PIPE, dg::f16_pipe_launchers, 2, dg::f16_o32_pipe_launchers},
     {"f32_256x128_pipe3_mfma32x32x2", DG_F32, 256, 128, 8, PIPE, dg::f32_pipe_launchers, 0},
     {"f32_256x256_pipe4_w8_mfma32x32x2", DG_F32, 256, 256, 4, PIPE, dg::f32_pipe_launchers, 1},
     {"f32_128x128_pipe4_mfma32x32x2", DG_F32, 128, 128, 8, PIPE, dg::f32_pipe_launchers, 2},
     {"bf16_64x64_simple", DG_BF16_F32ACC, 64, 64, 1, SIMPLE, nullptr, 0},
     {"bf16_128x128_pipe4_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 0, dg::bf16_o32_pipe_launchers},
-    {"bf16_256x128_pipe3_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1, dg::bf16_o32_pipe_launchers},
+    {"bf16_256x128_pipe2_w8_mfma32x32x16", DG_BF16_F32ACC, 256, 128, 4, PIPE, dg::bf16_pipe_launchers, 1, dg::bf16_o32_pipe_launchers},
     {"bf16_128x128_pipe2_ksplit2_mfma32x32x16", DG_BF16_F32ACC, 128, 128, 4, PIPE, dg::bf16_pipe_launchers, 2, dg::bf16_o32_pipe_launchers},
     {"f16_64x64_pipe4_ksplit2_mfma32x32x16", DG_F16_F32ACC, 64, 64, 4, PIPE, dg::f16_pipe_launchers, 3, dg::f16_o32_pipe_launchers},
     {"f16_128x32_pipe4_mfma32x32x16", DG_F16_F32ACC, 128, 32, 4, PIPE, dg::f16_pipe_launchers, 4, dg::f16_o32_pipe_launchers},
@@ -320,34 +320,32 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // a single K slab: writing C dominates, the large tile fills the GPU
         // once there is one per CU (attention's Q K^T, measured)
         if (K <= 64 && big >= 256) return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
-        // The tiles of one workgroup per CU run in waves of 256.  Once the
-        // 256x256 tiles fill more than half the CUs, the 256x128 tiles need
-        // two waves where the 256x256 tiles need one, and the 256x256 kernel
-        // does a tile's work at 15-30% less time per flop (measured 3072^3 to
-        // 8192^3 and 2304-4096 x 4096 x 512-16384: faster in every case but
-        // one tie at 6144^3 nt, where 2.25 waves round up against 4.5).
-        // Past one full round of 256x256 tiles, the tile by its cost in
-        // rounds: a full round of 256x256 tiles takes 3.125 times one of
-        // 128x128 tiles (4096^3, K from 1024 to 6144), and a partly filled
-        // last round about 0.6 of a full one for either tile.  A few tiles
-        // past a full round then favour 128x128: 4608x4096x4096 183-189 us
-        // against 196-201, 4096x4224x4096 179-186 against 197-202 (all three
-        // transpose pairs), while 5120^2x1024 (1.56 rounds), 6144^3 (2.25)
-        // and 7168^2x1024 (3.06) keep 256x256, 10-30% faster there.
-        const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256) * nb;
-        if (t256 > 256) {
-            auto rounds = [](int64_t t) { return (double)(t / 256) + (t % 256 ? 0.6 : 0.0); };
-            if (rounds(small) < 3.125 * rounds(t256)) return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
-        }
-        if (t256 > 128) return bf ? K_BF16_PIPE_256x256 : K_F16_PIPE_256x256;
-        // 256x128 tiles on more than half the CUs: the 256x128 kernel, save
-        // for tn (both operands through transposed LDS reads), where the
-        // 128x128 kernel with two K groups was 13-16% faster (2048 x 3072-4096
-        // x 4096).  The two-workgroup 128x128 kernel measured slower than the
+        // More than half the CUs with a 256x128 tile: the tile by its time in
+        // rounds.  Each of these kernels runs one workgroup per CU, so the
+        // tiles go in rounds of 256, and a partly filled last round costs
+        // about 0.82 of a full one.  A round takes a fixed part (launch,
+        // prologue, K-group sum, epilogue) and a part per unit of K: 128x128
+        // 4.67 us + 7.52 ns per k, 256x128 7.07 us + 14.78 ns, 256x256 16.29
+        // us + 21.44 ns, a least-squares fit to the times of the three tiles
+        // at 39 shapes (1536-8448 x 1024-8192 x 512-8192, all three transpose
+        // pairs; 5% rms error).  Over those 111 cases the tile chosen was
+        // within 3% of the fastest of the four in 108, and 5-9% slower in
+        // three (7168^2x1024 nn, nt; 4096^2x512 nn).  Examples: 4096^3, 6144^3
+        // and 8448x4096x2048 take 256x256, 2048x4096x4096, 2304x2048^2 and
+        // 4608^2x2048 take 256x128, 4608x4096x4096, 4224^3 and
+        // 5120x4096x2048 take 128x128 (a few 256x256 tiles past a round).
+        // The two-workgroup 128x128 kernel measured slower than the
         // one-workgroup one at every such shape and is not chosen.
         if (big > 128) {
-            if (ta && !tb) return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
-            return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
+            auto rounds = [](int64_t t) { return (double)(t / 256) + (t % 256 ? 0.82 : 0.0); };
+            const double k = (double)K;
+            const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256) * nb;
+            const double c256x256 = rounds(t256) * (16.29 + 0.02144 * k);
+            const double c256x128 = rounds(big) * (7.07 + 0.01478 * k);
+            const double c128 = rounds(small) * (4.67 + 0.00752 * k);
+            if (c128 < c256x128 && c128 < c256x256) return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
+            if (c256x128 < c256x256) return bf ? K_BF16_PIPE_256 : K_F16_PIPE_256;
+            return bf ? K_BF16_PIPE_256x256 : K_F16_PIPE_256x256;
         }
         // fewer 128x128 tiles than half the CUs and K too short to split:
         // smaller tiles (the LoRA K = 32 products, measured)

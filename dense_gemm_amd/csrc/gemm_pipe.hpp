@@ -538,11 +538,16 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     // consumed one step earlier.  The prologue issues the slabs the first
     // step does not issue itself.
     constexpr bool LAG2 = HALF && STAGES >= 4 && BM >= 128 && BN >= 128;
-    // 16-bit 256 x 256 tiles (eight 128 x 64 waves): fragments double-buffered
-    // per 16-wide k step instead of per slab (the slab-wide sets do not fit
-    // beside 128 accumulators), two stages; the prologue issues slab 0 only
-    constexpr bool FINE = HALF && BM == 256 && BN == 256;
-    static_assert(!FINE || (STAGES == 2 && KSPLIT == 1), "the 256 x 256 loop uses two stages");
+    // 16-bit 256 x 256 tiles (eight 128 x 64 waves) and 256 x 128 tiles
+    // (eight 64 x 64 waves): fragments double-buffered per 16-wide k step
+    // instead of per slab (the slab-wide sets do not fit beside 128
+    // accumulators, and beside 64 they filled the 256 registers of a lane and
+    // spilled), two stages; the prologue issues slab 0 only.  The 256 x 128
+    // tile measured 3.4-10.2% faster this way than with three stages and
+    // slab-wide sets for nn (2048-8192 x 1024-4096), -6.0% to +4.3% for nt,
+    // bit-identical.
+    constexpr bool FINE = HALF && BM == 256 && (BN == 256 || BN == 128);
+    static_assert(!FINE || (STAGES == 2 && KSPLIT == 1), "the 256-row 16-bit loop uses two stages");
     constexpr int PRO = FINE ? 1 : ((HALF && !LAG2) ? STAGES : STAGES - 1);
 #pragma unroll
     for (int s = 0; s < PRO; ++s) {
@@ -585,7 +590,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
         if (nk > 1) issue_slab(1, smem + STAGE_BYTES);
         bool pend = false;                      // B's loads of a slab deferred to k step 0
         lds_char_t *pdst = smem;
-        for (int kt = 0; kt < nk; ++kt) {
+        // FAST (a std::integral_constant): B's loads of this slab were
+        // deferred by the previous step and the slab this step refills is a
+        // whole slab before the last, so neither needs a test
+        auto fine_step = [&](auto fast_tag, int kt) {
+            constexpr bool FAST = decltype(fast_tag)::value;
             const lds_char_t *sA = smem + (kt % STAGES) * STAGE_BYTES;
             const lds_char_t *sB = sA + OpA::BYTES;
 #pragma unroll
@@ -599,14 +608,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                         if (s == 0) {
 #pragma unroll
                             for (int l = 0; l < OpB::LOADS; ++l)
-                                if (l * NL / OpB::LOADS == f && pend) gb.issue_one(pdst + OpA::BYTES, wave, l);
+                                if (l * NL / OpB::LOADS == f && (FAST || pend)) gb.issue_one(pdst + OpA::BYTES, wave, l);
                         }
                         if (f < TM) fa[nxt][f] = ga.frag(sA, wm0 + 32 * f, kk0 + s + 1, lane);
                         else if (f < TM + TN) fb[nxt][f - TM] = gb.frag(sB, wn0 + 32 * (f - TM), kk0 + s + 1, lane);
                         acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                if (s == 0 && pend) gb.advance();
+                if (s == 0 && (FAST || pend)) gb.advance();
             }
             wait_vmcnt<0>();
             __syncthreads();
@@ -614,8 +623,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             lds_char_t *dst = smem + (kt % STAGES) * STAGE_BYTES;   // slab n2's stage (two stages)
             const lds_char_t *rA = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
             const lds_char_t *rB = rA + OpA::BYTES;
-            const bool spread = n2 < nk && !(n2 == nk - 1 && krem < BK);
-            if (n2 < nk && !spread) issue_slab(n2, dst);
+            const bool spread = FAST ? true : (n2 < nk && !(n2 == nk - 1 && krem < BK));
+            if constexpr (!FAST) {
+                if (n2 < nk && !spread) issue_slab(n2, dst);
+            }
             constexpr int cur = (KPW - 1) & 1, nxt = cur ^ 1;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -633,7 +644,17 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             if (spread) ga.advance();
             pend = spread;
             pdst = dst;
-        }
+        };
+        // Step 0 (nothing deferred yet), then the steady state in a loop of
+        // its own (steps 1 .. whole slabs - 3), then the last steps: as in
+        // the loops below, bit-identical, and measured against the general
+        // step alone on one machine 1-3.4% faster at 3072^3 to 8192^3 (fp16
+        // and bf16) and 17% at 4096^2x512 nn.
+        int kt = 0;
+        if (nk > 0) fine_step(std::false_type(), kt++);
+        const int nfast = (krem == BK ? nk : nk - 1) - 2;
+        for (; kt < nfast; ++kt) fine_step(std::true_type(), kt);
+        for (; kt < nk; ++kt) fine_step(std::false_type(), kt);
     } else if constexpr (HALF) {
         // Two fragment sets, the loop unrolled by two so that each set stays
         // in fixed registers.  The next slab's LDS reads are unconditional:
@@ -705,12 +726,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             // The next slab's fragments are read between this slab's MFMAs,
             // one before each (order pinned by sched_barrier), rather than as
             // one block before them: each read then overlaps an MFMA.  Measured
-            // on the tiles with one fragment per MFMA (128 x 128 with two K
-            // groups, 256 x 128): 2-13% faster, except 256 x 128 tn (both
-            // operands through transposed reads), 6% slower, which keeps the
-            // block; the narrow tiles showed no difference and keep it too.
+            // on the 128 x 128 tile with two K groups, which has one fragment
+            // per MFMA: 2-13% faster; the narrow tiles showed no difference
+            // and keep the block.
             constexpr int NF = KPW * (TM + TN);
-            constexpr bool SPLITRD = NF == KPW * TM * TN && !(BM == 256 && TA && !TB);
+            constexpr bool SPLITRD = NF == KPW * TM * TN;
             if constexpr (!SPLITRD) read(kt + 1, na, nb);
             const lds_char_t *rA = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
             const lds_char_t *rB = rA + OpA::BYTES;
@@ -758,16 +778,12 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
         // Results are bit-identical (the same operations in the same order).
         // Measured against the general step alone, one machine: fp16 and bf16
         // 2048^3 1.5-5.3% faster, 512x5632x2048 4.5-6.2%, 2048^2x8192
-        // 5-12%, the 64x64 tile at 1024^2x4096 tn and nt 8-13%.  The 256x128
-        // tile keeps the general loop: its 256 registers per lane are already
-        // full, and the second copy of the step spilled there (nn +62%).
+        // 5-12%, the 64x64 tile at 1024^2x4096 tn and nt 8-13%.
         int kt = 0;
-        if constexpr (!(BM == 256 && BN == 128)) {
-            const int nfast = (krem == BK ? nk : nk - 1) - PRO;
-            for (; kt + 1 < nfast; kt += 2) {
-                step(std::true_type(), kt, fa0, fb0, fa1, fb1);
-                step(std::true_type(), kt + 1, fa1, fb1, fa0, fb0);
-            }
+        const int nfast = (krem == BK ? nk : nk - 1) - PRO;
+        for (; kt + 1 < nfast; kt += 2) {
+            step(std::true_type(), kt, fa0, fb0, fa1, fb1);
+            step(std::true_type(), kt + 1, fa1, fb1, fa0, fb0);
         }
         for (; kt < nk; kt += 2) {
             step(std::false_type(), kt, fa0, fb0, fa1, fb1);

@@ -59,7 +59,7 @@ const launch_fn *pipe16_table(int config)
 {
     static const launch_fn table[9][4] = {
         DG_PIPE4(T, TC, 128, 128, 64, 64, 4, 2, 16),
-        DG_PIPE4(T, TC, 256, 128, 64, 64, 3, 1, 16),
+        DG_PIPE4(T, TC, 256, 128, 64, 64, 2, 1, 16),
         DG_PIPE4(T, TC, 128, 128, 64, 64, 2, 2, 16),
         DG_PIPE4(T, TC, 64, 64, 64, 32, 4, 2, 16),
         DG_PIPE4(T, TC, 128, 32, 32, 32, 4, 1, 16),

@@ -182,28 +182,26 @@ def test_underfilled_16bit_grids_take_64x64_tiles_unsplit():
 
 def test_16bit_large_grids_take_the_tile_that_fills_the_cus_in_one_wave():
     for dtype in (1, 2):
-        # more than 128 tiles of 256x256: the 256x256 kernel, every transpose pair
-        for M, N, K in ((4096, 4096, 4096), (3072, 3072, 3072), (8192, 8192, 1024), (2304, 4096, 2048),
-                        (6144, 6144, 6144)):
-            for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
-                k = dg.dg_select_kernel(ta, tb, M, N, K, 256, M if ta else K, 256, K if tb else N, 256, N,
-                                        dtype)
-                assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (256, 256), (M, N, K, ta, tb)
-        # a few 256x256 tiles past one full round of the CUs: 128x128, whose
-        # last round is the smaller loss; more rounds keep 256x256
-        for M, N, K, tile in ((4608, 4096, 4096, (128, 128)), (4096, 4224, 4096, (128, 128)),
-                              (4096, 4104, 1032, (128, 128)), (5120, 4096, 2048, (256, 256)),
-                              (5120, 5120, 1024, (256, 256)), (7168, 7168, 1024, (256, 256)),
-                              (8192, 8192, 8192, (256, 256))):
+        # the tile with the least time in rounds of 256 workgroups (a round: a
+        # fixed part and a part per unit of K; a partly filled round counting
+        # 0.82); each of these was the fastest tile when measured, every
+        # transpose pair
+        for M, N, K, tile in ((4096, 4096, 4096, (256, 256)), (3072, 3072, 3072, (256, 256)),
+                              (8192, 8192, 2048, (256, 256)), (6144, 6144, 6144, (256, 256)),
+                              (1536, 8192, 2048, (256, 256)), (5120, 5120, 1024, (256, 256)),
+                              (3000, 3000, 3000, (256, 256)), (3584, 3584, 3584, (256, 256)),
+                              (2048, 4096, 4096, (256, 128)), (2560, 2560, 2560, (256, 128)),
+                              (2304, 2048, 2048, (256, 128)), (8192, 1024, 1024, (256, 128)),
+                              (4096, 2048, 4096, (256, 128)), (8448, 4096, 2048, (256, 256)),
+                              (6400, 6400, 2048, (256, 256)), (5120, 4096, 2048, (128, 128)),
+                              (4608, 4608, 2048, (256, 128)), (4608, 4096, 4096, (128, 128)),
+                              (4096, 4224, 4096, (128, 128)), (4224, 4224, 4224, (128, 128)),
+                              (4096, 4608, 1024, (128, 128)),
+                              (4352, 4096, 4096, (128, 128))):
             for ta, tb in ((0, 0), (1, 0), (0, 1)):
                 k = dg.dg_select_kernel(ta, tb, M, N, K, 256, M if ta else K, 256, K if tb else N, 256, N,
                                         dtype)
                 assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == tile, (M, N, K, ta, tb)
-        # 129-256 tiles of 256x128: 256x128 except tn, which keeps 128x128
-        for M, N, K in ((2048, 4096, 4096), (2560, 2560, 4096), (8192, 1024, 1024)):
-            assert tile_of(M, N, K, dtype) == (256, 128), (M, N, K)
-            k = dg.dg_select_kernel(1, 0, M, N, K, 256, M, 256, N, 256, N, dtype)
-            assert (dg.dg_kernel_tile_m(k), dg.dg_kernel_tile_n(k)) == (128, 128), (M, N, K)
         # at most 128 such tiles: 128x128
         assert tile_of(2048, 2048, 2048, dtype) == (128, 128)
         assert tile_of(2048, 2048, 8192, dtype) == (128, 128)
@@ -369,5 +367,5 @@ def test_ex_forced_kernel_checks():
 def test_bf16_kernels_listed():
     names = dg.kernel_names()
     for n in ("bf16_64x64_simple", "bf16_128x128_pipe4_ksplit2_mfma32x32x16",
-              "bf16_256x128_pipe3_w8_mfma32x32x16", "bf16_256x256_pipe2_w8_mfma32x32x16"):
+              "bf16_256x128_pipe2_w8_mfma32x32x16", "bf16_256x256_pipe2_w8_mfma32x32x16"):
         assert n in names
