@@ -1,6 +1,7 @@
 """Build libdense_gemm_amd.so for gfx950 with hipcc, in place.
 
-    python dense_gemm_amd/build.py
+    python dense_gemm_amd/build.py                # build
+    python dense_gemm_amd/build.py --resources    # registers, scratch, LDS per kernel
 
 (run by path: importing the package would load the library being rebuilt)
 
@@ -69,6 +70,55 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# ---- register, scratch and LDS use of every kernel ------------------------
+# The compiler's resource-usage remarks (-Rpass-analysis=kernel-resource-usage)
+# for a device-only compile of each kernel source: the VGPR, AGPR and SGPR
+# counts, scratch bytes per lane, spills, occupancy and LDS of every kernel.
+_RES_KEYS = {"TotalSGPRs": "sgpr", "VGPRs": "vgpr", "AGPRs": "agpr",
+             "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy",
+             "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill", "LDS Size [bytes/block]": "lds"}
+
+
+def _resources_of(src: str) -> list:
+    cmd = [HIPCC] + FLAGS + ["--cuda-device-only", "-c", "-Rpass-analysis=kernel-resource-usage",
+                             os.path.join(CSRC, src), "-o", os.devnull]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    rows, cur = [], None
+    for line in r.stderr.splitlines():
+        if "remark:" not in line:
+            continue
+        text = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+        if text.startswith("Function Name:"):
+            cur = {"source": src, "kernel": text.split(":", 1)[1].strip()}
+            rows.append(cur)
+        elif cur is not None and ":" in text:
+            key, val = text.rsplit(":", 1)
+            if key.strip() in _RES_KEYS:
+                v = val.strip()
+                cur[_RES_KEYS[key.strip()]] = int(v) if v.lstrip("-").isdigit() else v
+    return rows
+
+
+def resources() -> list:
+    """Resource use of every kernel of the library, one dict per kernel."""
+    srcs = [s for s in SOURCES if s.endswith(".hip")]
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        return [row for rows in ex.map(_resources_of, srcs) for row in rows]
+
+
+def resources_table(rows: list) -> str:
+    cols = ["vgpr", "agpr", "sgpr", "scratch", "vgpr_spill", "sgpr_spill", "occupancy", "lds"]
+    out = ["| source | kernel | " + " | ".join(cols) + " |", "|---|---|" + "---|" * len(cols)]
+    for r in rows:
+        out.append(f"| {r['source']} | `{r['kernel']}` | " + " | ".join(str(r.get(c, "")) for c in cols) + " |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "--resources":
+        print(resources_table(resources()))
+    else:
+        build()
     sys.exit(0)
