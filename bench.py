@@ -47,8 +47,11 @@ HBM_PEAK = 8000.0     # GB/s
 # Control benchmarks and their references.  "Metal GEMM Kernels for LoRA
 # Training on Apple Silicon", section 9: a performance figure is trusted only
 # while a control benchmark stays within 10% of its reference.  The matrix-core
-# probes' references are the published peaks; the copy's is the read + write
-# rate a plain copy sustains on this part (4.6 TB/s of the 8 TB/s peak).
+# probes' references are the published peaks.  No figure is published for what
+# a plain copy sustains (a read + write stream does not approach the 8 TB/s HBM
+# peak), so the copy's reference is the rate measured here: 4.47-4.67 TB/s on
+# every box this library was measured on, 56-58% of the peak.  The line also
+# reports the copy as a fraction of the peak.
 REF_MFMA_F32 = PEAK_F32
 REF_MFMA_F16 = PEAK_F16
 REF_COPY_GBS = 4600.0
@@ -225,7 +228,7 @@ def control_probes(dev, stream):
           and gbs >= (1 - CONTROL_TOL) * REF_COPY_GBS)
     return {"mfma_f32_tflops": res["mfma_f32"]["tflops"], "mfma_f32_clock_mhz": res["mfma_f32"]["clock_mhz"],
             "mfma_f16_tflops": res["mfma_f16"]["tflops"], "mfma_f16_clock_mhz": res["mfma_f16"]["clock_mhz"],
-            "copy_gbs": round(gbs, 1),
+            "copy_gbs": round(gbs, 1), "copy_frac_of_hbm_peak": round(gbs / HBM_PEAK, 3),
             "references": {"mfma_f32_tflops": REF_MFMA_F32, "mfma_f16_tflops": REF_MFMA_F16,
                            "copy_gbs": REF_COPY_GBS, "tolerance": CONTROL_TOL},
             "within_tolerance": bool(ok)}
