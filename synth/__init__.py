@@ -203,6 +203,13 @@ LORA_GEMMS = [
 ]
 
 
+# The products of the step that come in pairs of one shape with separate
+# outputs, by index into LORA_GEMMS: gate/up, the two rank-32 "+=" updates,
+# dBg/dBu, dAg/dAu.  One strided-batch launch can run each pair (the two
+# "dH +=" and "dX +=" products write one output per pair, so they cannot).
+LORA_PAIRS = ((0, 1), (5, 6), (12, 13), (14, 15))
+
+
 def lora_problem(index: int, seed: int = 3, out: str = "f16"):
     """Logical fp16 operands of one LoRA-step GEMM (and C0 when beta != 0,
     rounded to `out`, the type of C: "f16", or "f32" for the fp32-output

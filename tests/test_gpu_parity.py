@@ -282,6 +282,36 @@ def test_lora_step_gemm(dg, index):
     print(f"LoRA GEMM {name}: max err/bound {worst:.4f}", flush=True)
 
 
+@pytest.mark.parametrize("pair", synth.LORA_PAIRS)
+def test_lora_pair_strided_batch(dg, pair):
+    # two LoRA products of one shape, stored one after the other, in one
+    # strided-batch launch: every output of both against the oracle
+    import torch
+    i0, i1 = pair
+    name, M, N, K, ta, tb, beta, _ = synth.LORA_GEMMS[i0]
+    assert synth.LORA_GEMMS[i1][1:7] == (M, N, K, ta, tb, beta)
+    probs = [synth.lora_problem(i, seed=3) for i in pair]
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(np.stack([np.ascontiguousarray(a.T if ta else a) for a, _, _ in probs])).to(dev)
+    B = torch.from_numpy(np.stack([np.ascontiguousarray(b.T if tb else b) for _, b, _ in probs])).to(dev)
+    if beta != 0.0:
+        C = torch.from_numpy(np.stack([c0 for _, _, c0 in probs])).to(dev)
+    else:
+        C = torch.full((2, M, N), float("nan"), dtype=torch.float16, device=dev)
+    lda, ldb = (M if ta else K), (K if tb else N)
+    print(f"LoRA pair {name} and {synth.LORA_GEMMS[i1][0]} ({M}x{N}x{K}), batch 2", flush=True)
+    rc = dg.dg_gemm_ex(ta, tb, M, N, K, 1.0, A.data_ptr(), lda, M * K, B.data_ptr(), ldb, K * N, beta,
+                       C.data_ptr(), N, M * N, 2, None, dg.DG_EPI_NONE, dg.DG_F16_F32ACC,
+                       torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, dg.dg_status_string(rc)
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy().astype(np.float64)
+    for h, (a, b, c0) in enumerate(probs):
+        ref, ab = oracle.gemm(False, False, M, N, K, 1.0, a, K, b, N, beta, c0, N)
+        worst, bad = oracle.compare("f16", got[h], ref, ab, 1.0, beta, c0)
+        assert bad == 0, f"{synth.LORA_GEMMS[pair[h]][0]}: {bad} out of bound, max err/bound {worst:.3g}"
+
+
 # ---------------------------------------------------------------------------
 # split-K: fp32 partials in a caller workspace, then one reduction
 # ---------------------------------------------------------------------------
