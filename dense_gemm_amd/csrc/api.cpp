@@ -98,6 +98,7 @@ const Family kFamilies[] = {
     {"f32_64x64_pipe4_mfma32x32x2", DG_F32, 64, 64, 8, PIPE, dg::f32_pipe_launchers, 6},
     {"f32_128x64_pipe4_dw_mfma32x32x2", DG_F32, 128, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 7},
     {"f32_64x64_pipe4_dw_mfma32x32x2", DG_F32, 64, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 8},
+    {"f32_64x64_pipe3_k32_mfma32x32x2", DG_F32, 64, 64, 8, PIPE, dg::f32_pipe_launchers, 9},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -109,7 +110,7 @@ enum {
     K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23, K_F32_PIPE_256x128_DW = 24,
     K_F32_PIPE_128_DW = 25, K_F16_PIPE_128_DW = 26, K_F16_PIPE_64_DW = 27, K_BF16_PIPE_128_DW = 28,
     K_BF16_PIPE_64_DW = 29, K_BF16_128 = 30, K_BF16_256 = 31, K_F32_PIPE_128x64 = 32,
-    K_F32_PIPE_64 = 33, K_F32_PIPE_128x64_DW = 34, K_F32_PIPE_64_DW = 35
+    K_F32_PIPE_64 = 33, K_F32_PIPE_128x64_DW = 34, K_F32_PIPE_64_DW = 35, K_F32_PIPE_64_K32 = 36
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -303,8 +304,22 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         }
         static const int pipe16[4] = {K_F32_PIPE_256x128, K_F32_PIPE_128, K_F32_PIPE_128x64, K_F32_PIPE_64};
         static const int pipe4[4] = {K_F32_PIPE_256x128_DW, K_F32_PIPE_128_DW, K_F32_PIPE_128x64_DW, K_F32_PIPE_64_DW};
-        if (pipe) return pipe16[pk];
+        if (pipe) {
+            // The 64x64 tile with 32-deep slabs (each k-contiguous row of a
+            // stage one whole 128-byte line) in three stages, 48 KB of LDS, so
+            // three workgroups per CU.  Against the 16-deep four-stage kernel
+            // (32 KB, four resident per CU), one machine: 512^3 7-9% faster,
+            // 1024^3 7-9%, 1024^2x4096 and 512^2x8192 8-10%, 8192x256x8192
+            // (ld + 8) 3-6% for nn, nt and tt (tn even), 2304x2048^2 5-10%,
+            // 3072^3 4-5%.  Grids of 769 to 1024 tiles fill one round of four
+            // per CU but need two of three: there the 16-deep kernel stays
+            // (2048^3 and 2048^2x1024 nt, tn, tt 3-19% slower on the 32-deep
+            // one, 1792^2x2048 2-4%).
+            if (pk == 3 && (t64 <= 768 || t64 > 1024)) return K_F32_PIPE_64_K32;
+            return pipe16[pk];
+        }
         // rows not 16-byte aligned: the same tiles with 4-byte direct loads
+        // (the 32-deep slab measured 38% slower with them: 4095x4097x1031)
         if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return pipe4[pk];
         return big >= 384 ? K_F32_256 : K_F32_128;
     }

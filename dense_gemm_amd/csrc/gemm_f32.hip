@@ -35,6 +35,8 @@ const launch_fn *f32_launchers(int config)
 //      128x128 tile to give every compute unit one: tall-skinny outputs)
 //   6: 64x64 tile, 4 stages, 4 waves of 32x32 (two or more workgroups per CU)
 //   7, 8: configs 5 and 6 with 4-byte direct loads
+//   9: 64x64 tile, 3 stages of 32-deep slabs (128-byte k-contiguous rows),
+//      4 waves of 32x32 (three workgroups per CU)
 #define DG_PIPE4(BM, BN, WM, WN, ST)                                                                \
     {launch_pipe<float, BM, BN, WM, WN, false, false, ST, 1>, launch_pipe<float, BM, BN, WM, WN, false, true, ST, 1>, \
      launch_pipe<float, BM, BN, WM, WN, true, false, ST, 1>, launch_pipe<float, BM, BN, WM, WN, true, true, ST, 1>}
@@ -43,7 +45,7 @@ const launch_fn *f32_launchers(int config)
      launch_pipe<float, BM, BN, WM, WN, true, false, ST, 1, 4>, launch_pipe<float, BM, BN, WM, WN, true, true, ST, 1, 4>}
 const launch_fn *f32_pipe_launchers(int config)
 {
-    static const launch_fn table[9][4] = {
+    static const launch_fn table[10][4] = {
         {launch_pipe<float, 256, 128, 128, 64, false, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, false, true, 3, 1>,
          launch_pipe<float, 256, 128, 128, 64, true, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, true, true, 3, 1>},
         {launch_pipe<float, 256, 256, 128, 64, false, false, 4, 1>, launch_pipe<float, 256, 256, 128, 64, false, true, 4, 1>,
@@ -56,6 +58,10 @@ const launch_fn *f32_pipe_launchers(int config)
         DG_PIPE4(64, 64, 32, 32, 4),
         DG_PIPE4DW(128, 64, 64, 32, 4),
         DG_PIPE4DW(64, 64, 32, 32, 4),
+        {launch_pipe<float, 64, 64, 32, 32, false, false, 3, 1, 16, float, 32>,
+         launch_pipe<float, 64, 64, 32, 32, false, true, 3, 1, 16, float, 32>,
+         launch_pipe<float, 64, 64, 32, 32, true, false, 3, 1, 16, float, 32>,
+         launch_pipe<float, 64, 64, 32, 32, true, true, 3, 1, 16, float, 32>},
     };
     return table[config];
 }

@@ -6,7 +6,7 @@
 //   fp16 / bf16: v_mfma_f32_32x32x16_f16 / _bf16 with fp32 accumulators
 //   ("Metal GEMM Kernels for LoRA Training on Apple Silicon", section 1: the
 //   fp32 accumulator keeps the fast path), K slabs of 64;
-//   fp32: v_mfma_f32_32x32x2_f32, K slabs of 16.
+//   fp32: v_mfma_f32_32x32x2_f32, K slabs of 16 (32 on one 64 x 64 kernel).
 //   The bias and activation are the fused epilogue of "From a C loop to a GPU
 //   kernel", "Fusion"; grid y is the batch of a strided-batched call (the
 //   per-head offsets of "Metal GEMM Kernels for LoRA Training", section 8).
@@ -40,13 +40,15 @@
 //     own m (or n) -- the MFMA operand layout -- with no write-side transpose
 //     (the page's section 3 transposes on the write; gfx950 can do it on the
 //     read).
-// fp32 LDS layouts: k-contiguous operand [BMN][16] floats, 64-byte rows, the
-// 16-byte chunk c of row r at chunk c ^ ((r>>2)&3); one ds_read_b128 gives a
-// lane 4 consecutive k (4 MFMA steps).  m/n-contiguous operand [16][BMN]
-// floats, the 128-byte chunk q of row k at q ^ ((k>>3)&1); a lane reads one
-// float per MFMA step, the two half-waves from rows k and k+8 (different
-// bank halves after the swizzle).  In both types lane half h of MFMA step s
-// takes k = h*BK/2 + s, the same for both operands.
+// fp32 LDS layouts, K slab BK = 16 or 32: k-contiguous operand [BMN][BK]
+// floats, rows of 64 or 128 bytes, the 16-byte chunk c of row r at chunk
+// c ^ ((r>>2)&3) (BK = 16) or c ^ (r&7) ^ ((r>>3)&1) (BK = 32); one
+// ds_read_b128 gives a lane 4 consecutive k (4 MFMA steps).  m/n-contiguous
+// operand [BK][BMN] floats, the 128-byte chunk q of row k at
+// q ^ ((k/(BK/2))&1); a lane reads one float per MFMA step, the two
+// half-waves from rows k and k+BK/2 (different bank halves after the
+// swizzle).  In both types lane half h of MFMA step s takes k = h*BK/2 + s,
+// the same for both operands.
 // The swizzle is applied by choosing which global address each lane fetches,
 // since a direct load writes its lanes contiguously.
 //
@@ -305,16 +307,34 @@ struct PipeOperandH {
 };
 
 
-// One fp32 operand of the pipelined kernel (K slab 16).
+// One fp32 operand of the pipelined kernel (K slab BKS: 16 or 32).
 //   KCONT: stored [ext][K] (k contiguous); else stored [K][ext].
 //   LB: bytes per lane per direct load: 16, or 4 for rows that are not
 //   16-byte aligned (any fp32 layout).  The LDS layout is the same; a
 //   4-byte load fills a quarter of the bytes a 16-byte load does, and each
 //   lane fetches the element that belongs at its LDS slot.
-template <int BMN, bool KCONT, int NW, int LB = 16>
+//   BKS: a slab of 32 makes each k-contiguous row of a stage one whole
+//   128-byte line (64 bytes, half a line, at 16).
+template <int BMN, bool KCONT, int NW, int LB = 16, int BKS = 16>
 struct PipeOperandS {
     static_assert(LB == 16 || LB == 4, "16- or 4-byte direct loads");
-    static constexpr int BK = 16;
+    static_assert(BKS == 16 || BKS == 32, "slabs of 16 or 32 k");
+    static constexpr int BK = BKS;
+    static constexpr int CH = BK / 4;                      // 16-byte chunks of a k-contiguous row
+    static constexpr int HK = BK / 2;                      // k rows read by one half-wave
+    // Chunk swizzle of k-contiguous row r.  A fragment read has lane l read
+    // row b0 + l%32 at one logical chunk; the swizzle spreads 8 consecutive
+    // rows over the 8 chunks of 128 bytes, and 16 consecutive rows over the
+    // 16 of 256 bytes (64-byte rows: 4 chunks, by (r >> 2) & 3 beside r & 1;
+    // 128-byte rows: 8 chunks, by r & 7, flipped for rows 8-15 of each 16).
+    static __device__ __forceinline__ int swz(int r)
+    {
+        return BK == 16 ? ((r >> 2) & 3) : ((r & 7) ^ ((r >> 3) & 1));
+    }
+    // Half swap of m/n-contiguous k row r: which 128-byte half of a 64-wide
+    // block row holds columns 0-31; the two half-waves (k rows HK apart)
+    // then read different halves.
+    static __device__ __forceinline__ int hsw(int r) { return (r / HK) & 1; }
     static constexpr int BYTES = BMN * BK * 4;            // one stage
     static constexpr int SPAN = 64 * LB;                   // LDS bytes of one wave-wide load
     static constexpr int LOADS = BYTES / (NW * SPAN);      // loads per thread per slab
@@ -339,15 +359,15 @@ struct PipeOperandS {
             if constexpr (LB == 16) {
                 const int rbase = (i * NW + wave) * ROWS_PER_LOAD;
                 if constexpr (KCONT) {
-                    const int r = rbase + (lane >> 2);
-                    const int c = (lane & 3) ^ ((r >> 2) & 3);    // logical 16-byte chunk (4 k)
+                    const int r = rbase + lane / CH;
+                    const int c = (lane % CH) ^ swz(r);           // logical 16-byte chunk (4 k)
                     int row = mn0 + r;
                     row = row < ext ? row : ext - 1;
                     off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4) * 4);
                 } else {
                     const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
                     const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
-                    const int q = (p >> 3) ^ ((r >> 3) & 1);          // logical 128-byte chunk
+                    const int q = (p >> 3) ^ hsw(r);                  // logical 128-byte chunk
                     int col = mn0 + q * 32 + (p & 7) * 4;
                     col = col < ext ? col : ext - 4;
                     off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
@@ -357,12 +377,12 @@ struct PipeOperandS {
                 const int r = b / ROW_BYTES, w = b % ROW_BYTES;
                 const int p = w >> 4, e = (w >> 2) & 3;               // 16-byte slot, element
                 if constexpr (KCONT) {
-                    const int c = p ^ ((r >> 2) & 3);
+                    const int c = p ^ swz(r);
                     int row = mn0 + r;
                     row = row < ext ? row : ext - 1;
                     off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4 + e) * 4);
                 } else {
-                    const int q = (p >> 3) ^ ((r >> 3) & 1);
+                    const int q = (p >> 3) ^ hsw(r);
                     int col = mn0 + q * 32 + (p & 7) * 4 + e;
                     col = col < ext ? col : ext - 1;
                     off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
@@ -383,8 +403,8 @@ struct PipeOperandS {
                 lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
                 int valid;  // floats of this 16-byte piece that lie before K
                 if constexpr (KCONT) {
-                    const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> 2);
-                    const int c = (lane & 3) ^ ((r >> 2) & 3);
+                    const int r = (i * NW + wave) * ROWS_PER_LOAD + lane / CH;
+                    const int c = (lane % CH) ^ swz(r);
                     valid = krem - c * 4;
                 } else {
                     const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
@@ -406,7 +426,7 @@ struct PipeOperandS {
                 const int b = (i * NW + wave) * SPAN + lane * 4;
                 const int r = b / ROW_BYTES, w = b % ROW_BYTES;
                 const int p = w >> 4, e = (w >> 2) & 3;
-                const int k = KCONT ? (p ^ ((r >> 2) & 3)) * 4 + e : r;   // this element's k
+                const int k = KCONT ? (p ^ swz(r)) * 4 + e : r;   // this element's k
                 *(__attribute__((address_space(3))) float *)(lds + b) = k < krem ? *src : 0.f;
             }
         }
@@ -431,7 +451,7 @@ struct PipeOperandS {
 
     // The operand values of MFMA steps 4*c2 .. 4*c2+3 for block rows
     // [b0, b0+32): lane l holds row (or column) b0 + l%32 and
-    // k = (l/32)*8 + 4*c2 + e, e = 0..3.
+    // k = (l/32)*HK + 4*c2 + e, e = 0..3.
     __device__ __forceinline__ f32x4 frag4(const lds_char_t *lds, int b0, int c2, int lane) const
     {
         typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
@@ -439,12 +459,12 @@ struct PipeOperandS {
         const int h = lane >> 5;
         if constexpr (KCONT) {
             const int r = b0 + (lane & 31);
-            const int c = 2 * h + c2;
-            const int p = c ^ ((r >> 2) & 3);
+            const int c = (CH / 2) * h + c2;
+            const int p = c ^ swz(r);
             return *(const lds_f32x4_t *)(lds + r * ROW_BYTES + p * 16);
         } else {
-            const int q = (b0 >> 5) ^ h;   // (k >> 3) & 1 == h for k = 8h + ...
-            const lds_char_t *base = lds + (8 * h + 4 * c2) * ROW_BYTES + q * 128 + (lane & 31) * 4;
+            const int q = (b0 >> 5) ^ h;   // hsw(k) == h for k = HK*h + ...
+            const lds_char_t *base = lds + (HK * h + 4 * c2) * ROW_BYTES + q * 128 + (lane & 31) * 4;
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = *(const lds_float_t *)(base + e * ROW_BYTES);
@@ -465,9 +485,10 @@ struct PipeOperandS {
 // SIMD from eight 64 x 64 sub-tiles instead (KSPLIT = 1).
 // LB: bytes per lane of each direct load, 16, or 4 for rows that are not
 // 16-byte aligned.  TC: the element type of C and the bias (T, or fp32 for an
-// fp32 output of 16-bit operands).
+// fp32 output of 16-bit operands).  FBK: the K slab of fp32 operands, 16 or
+// 32 (16-bit operands always take 64).
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
-          int LB = 16, typename TC = T>
+          int LB = 16, typename TC = T, int FBK = 16>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_pipe_kernel(GemmParams p)
 {
     constexpr bool HALF = sizeof(T) == 2;          // fp16 or bf16 operands
@@ -482,8 +503,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     static_assert(KPW >= 1 && KPW * KSPLIT == PIPE_BK / 16, "K split");
     static_assert(KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
     static_assert(HALF || KSPLIT == 1, "fp32 runs without K groups");
-    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW, LB>, PipeOperandS<BM, !TA, NW, LB>>::type OpA;
-    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW, LB>, PipeOperandS<BN, TB, NW, LB>>::type OpB;
+    static_assert(FBK == 16 || (!HALF && FBK == 32), "fp32 slabs of 16 or 32");
+    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW, LB>, PipeOperandS<BM, !TA, NW, LB, FBK>>::type OpA;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW, LB>, PipeOperandS<BN, TB, NW, LB, FBK>>::type OpB;
     constexpr int BK = OpA::BK;
     constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
     constexpr int SMEM = STAGES * STAGE_BYTES;
@@ -817,10 +839,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             }
             const lds_char_t *sA = smem + stage * STAGE_BYTES;
             const lds_char_t *sB = sA + OpA::BYTES;
-            constexpr int NM = 2 * 4 * TM * TN;
-            // 8 MFMA steps of k = 2 per slab, fragments 4 steps at a time
+            constexpr int NM = (BK / 2) * TM * TN;
+            // BK/2 MFMA steps of k = 2 per slab, fragments 4 steps at a time
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
+            for (int c2 = 0; c2 < BK / 8; ++c2) {
                 f32x4 a[TM], b[TN];
 #pragma unroll
                 for (int i = 0; i < TM; ++i) a[i] = ga.frag4(sA, wm0 + 32 * i, c2, lane);
@@ -855,12 +877,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
         // 8192x256x8192 7.6-12.5%, 512^3 8-13%, the 128x64 tile 3%, the
         // 128x128 tile 2.5-5.6% except nt, which was 0-24% slower
         // (6144^2x2048, 3072x4096^2, 5120x4096x2048) and keeps the general
-        // loop.  The 64x64 tile takes it on grids of at most 1024 workgroups
-        // (four per CU): above that it measured 3-22% slower at 2304x2048^2,
-        // 3000^3 and 3072^3 (4.5 to 9 workgroups per CU).
+        // loop.  The 64x64 tile takes it on grids whose workgroups are all
+        // resident at once: at most 1024 (four per CU) for 16-deep slabs,
+        // above which it measured 3-22% slower at 2304x2048^2, 3000^3 and
+        // 3072^3 (4.5 to 9 workgroups per CU); at most 768 (three per CU,
+        // 48 KB of LDS each) for 32-deep slabs.
         int kt = 0;
         if constexpr (!(BM == 128 && BN == 128 && !TA && TB)) {
-            const bool fast = !(BM == 64 && BN == 64) || gridDim.x * gridDim.y <= 1024;
+            const bool fast = !(BM == 64 && BN == 64) || gridDim.x * gridDim.y <= (FBK == 32 ? 768 : 1024);
             const int nfast = fast ? (krem == BK ? nk : nk - 1) - (STAGES - 1) : 0;
             for (; kt < nfast; ++kt) fstep(std::true_type(), kt);
         }
@@ -1075,13 +1099,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
-          int LB = 16, typename TC = T>
+          int LB = 16, typename TC = T, int FBK = 16>
 hipError_t launch_pipe(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT, LB, TC>,
+    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT, LB, TC, FBK>,
                            dim3(nwg, p.batch), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
 }
 
