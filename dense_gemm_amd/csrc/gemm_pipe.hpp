@@ -321,7 +321,9 @@ struct PipeOperandS {
     static_assert(BKS == 16 || BKS == 32, "slabs of 16 or 32 k");
     static constexpr int BK = BKS;
     static constexpr int CH = BK / 4;                      // 16-byte chunks of a k-contiguous row
+    static constexpr int CH_LOG = BK == 16 ? 2 : 3;
     static constexpr int HK = BK / 2;                      // k rows read by one half-wave
+    static constexpr int HK_LOG = BK == 16 ? 3 : 4;
     // Chunk swizzle of k-contiguous row r.  A fragment read has lane l read
     // row b0 + l%32 at one logical chunk; the swizzle spreads 8 consecutive
     // rows over the 8 chunks of 128 bytes, and 16 consecutive rows over the
@@ -334,7 +336,7 @@ struct PipeOperandS {
     // Half swap of m/n-contiguous k row r: which 128-byte half of a 64-wide
     // block row holds columns 0-31; the two half-waves (k rows HK apart)
     // then read different halves.
-    static __device__ __forceinline__ int hsw(int r) { return (r / HK) & 1; }
+    static __device__ __forceinline__ int hsw(int r) { return (r >> HK_LOG) & 1; }
     static constexpr int BYTES = BMN * BK * 4;            // one stage
     static constexpr int SPAN = 64 * LB;                   // LDS bytes of one wave-wide load
     static constexpr int LOADS = BYTES / (NW * SPAN);      // loads per thread per slab
@@ -359,8 +361,8 @@ struct PipeOperandS {
             if constexpr (LB == 16) {
                 const int rbase = (i * NW + wave) * ROWS_PER_LOAD;
                 if constexpr (KCONT) {
-                    const int r = rbase + lane / CH;
-                    const int c = (lane % CH) ^ swz(r);           // logical 16-byte chunk (4 k)
+                    const int r = rbase + (lane >> CH_LOG);
+                    const int c = (lane & (CH - 1)) ^ swz(r);     // logical 16-byte chunk (4 k)
                     int row = mn0 + r;
                     row = row < ext ? row : ext - 1;
                     off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4) * 4);
@@ -403,8 +405,8 @@ struct PipeOperandS {
                 lds_char_t *dst = lds + (i * NW + wave) * 1024 + lane * 16;
                 int valid;  // floats of this 16-byte piece that lie before K
                 if constexpr (KCONT) {
-                    const int r = (i * NW + wave) * ROWS_PER_LOAD + lane / CH;
-                    const int c = (lane % CH) ^ swz(r);
+                    const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane >> CH_LOG);
+                    const int c = (lane & (CH - 1)) ^ swz(r);
                     valid = krem - c * 4;
                 } else {
                     const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
@@ -459,12 +461,12 @@ struct PipeOperandS {
         const int h = lane >> 5;
         if constexpr (KCONT) {
             const int r = b0 + (lane & 31);
-            const int c = (CH / 2) * h + c2;
+            const int c = (h << (CH_LOG - 1)) + c2;
             const int p = c ^ swz(r);
             return *(const lds_f32x4_t *)(lds + r * ROW_BYTES + p * 16);
         } else {
             const int q = (b0 >> 5) ^ h;   // hsw(k) == h for k = HK*h + ...
-            const lds_char_t *base = lds + (HK * h + 4 * c2) * ROW_BYTES + q * 128 + (lane & 31) * 4;
+            const lds_char_t *base = lds + ((h << HK_LOG) + 4 * c2) * ROW_BYTES + q * 128 + (lane & 31) * 4;
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = *(const lds_float_t *)(base + e * ROW_BYTES);
