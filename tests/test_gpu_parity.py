@@ -106,6 +106,27 @@ def test_pipelined_kernels(dg, dtype, ta, tb, shape):
         check_full(p, kernel=k, out=out)
 
 
+@pytest.mark.parametrize("ta,tb", TRANS)
+@pytest.mark.parametrize("tiles_mn", [(24, 32), (25, 31), (32, 32), (33, 32)])
+def test_f32_64x64_steady_state_gates(dg, ta, tb, tiles_mn):
+    """The two fp32 64x64 kernels on grids at the bounds of their steady-state
+    loop, which runs only while every workgroup is resident: at most 768
+    workgroups with 32-deep slabs (three per CU), 1024 with 16-deep.  The four
+    grids (768, 775, 1024 and 1056 tiles) put each kernel on both sides of its
+    bound, so the loop without per-slab tests and the generic loop alone are
+    both compared with the oracle; ragged M and N, a partial last K slab."""
+    tm, tn = tiles_mn
+    M, N, K = 64 * tm - 8, 64 * tn - 4, 269
+    a, b, c0 = synth.problem(M, N, K, "f32", "uniform", 190 + 2 * ta + tb, with_c0=True)
+    pad = tuple((-x) % 4 + 4 for x in ((M if ta else K), (K if tb else N), N))
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, "f32", pad)
+    assert pipe_ok(p)
+    for name in ("f32_64x64_pipe3_k32_mfma32x32x2", "f32_64x64_pipe4_mfma32x32x2"):
+        k = dg.kernel_names().index(name)
+        print(f"kernel {name} tiles {tm}x{tn} ta={ta} tb={tb}", flush=True)
+        check_full(p, kernel=k)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_unaligned_pointers(dg, dtype):
     M, N, K = 129, 257, 77
