@@ -640,6 +640,66 @@ def f16_k_sweep(dev, stream, reps):
     return out
 
 
+def slab_probe(dev, stream, slabs=2000):
+    """The slab probe (libdense_gemm_probe.so, dgp_slab_probe): one workgroup
+    per CU doing the per-slab work of the fp16 2048^3 tile without its data
+    flow -- per SIMD and slab 8 KB of direct loads into LDS, 16 KB of
+    fragment reads from LDS and 16 MFMAs.  Shader cycles per slab: the median
+    over the workgroups of the first wave's s_memtime span, from the second
+    of two launches.
+      l2        each combination of the parts, loading contiguous 32 KB
+                windows of a 1 MiB source that stays in L2;
+      patterns  loads alone and all three parts for load patterns between
+                that and the GEMM's: contiguous or panel rows 4 KB apart (the
+                row stride of K = 2048 fp16 operands), 1, 6 or 12 groups per
+                XCD and slab (6 x 32 KB is the 2048^3 tiles' 192 KB of A and
+                B panels per XCD and slab), from a source that fits L2 or a
+                64 MiB one that fits only the Infinity Cache; all three
+                parts also with one slab of loads in flight at each slab's
+                start instead of two."""
+    import statistics
+    import torch
+
+    import dense_gemm_amd.probe as pr
+
+    sptr = stream.cuda_stream
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs, dtype=torch.int64, device=dev)
+    L, M, R = pr.DGP_SLAB_LOADS, pr.DGP_SLAB_MFMA, pr.DGP_SLAB_READS
+
+    def run(mode, windows, pitch, src):
+        for _ in range(2):
+            rc = pr.dgp_slab_probe(mode, wgs, slabs, windows, pitch, src.data_ptr(), src.numel() * 4,
+                                   sink.data_ptr(), clocks.data_ptr(), sptr)
+            if rc != 0:
+                raise RuntimeError(f"dgp_slab_probe failed ({rc}, hip {pr.dgp_last_hip_error()})")
+        torch.cuda.synchronize()
+        return round(statistics.median(int(x) for x in clocks.cpu().tolist()) / slabs, 1)
+
+    mib = 1 << 18                                                       # floats per MiB
+    small = torch.ones(mib, dtype=torch.float32, device=dev)
+    l2 = {name: run(mode, 1, 128, small) for name, mode in (
+        ("loads", L), ("mfma", M), ("reads", R), ("loads+mfma", L | M), ("loads+reads", L | R),
+        ("reads+mfma", R | M), ("loads+reads+mfma", L | R | M))}
+    del small
+    patterns = {}
+    # (name, windows, pitch, MiB): 8 groups of 1 MiB at pitch 4 KB = one
+    # fixed group per XCD, resident in its L2
+    for name, windows, pitch, size in (("contiguous, 1 group, L2", 1, 128, 1),
+                                       ("rows 4 KB apart, 1 group, L2", 1, 4096, 8),
+                                       ("contiguous, 6 groups, 64 MiB", 6, 128, 64),
+                                       ("rows 4 KB apart, 6 groups, 64 MiB", 6, 4096, 64),
+                                       ("rows 4 KB apart, 12 groups, 64 MiB", 12, 4096, 64)):
+        src = torch.ones(size * mib, dtype=torch.float32, device=dev)
+        D = pr.DGP_SLAB_DEPTH1
+        patterns[name] = {"loads": run(L, windows, pitch, src), "loads+reads+mfma": run(L | R | M, windows, pitch, src),
+                          "loads+reads+mfma, one slab in flight": run(L | R | M | D, windows, pitch, src)}
+        del src
+    return {"workgroups": wgs, "slabs": slabs, "mfma_cycles_per_slab_at_peak": 16 * 32,
+            "cycles_per_slab_l2": l2, "cycles_per_slab_by_load_pattern": patterns}
+
+
 def smi_clocks(index=0):
     """Clock state from `amd-smi metric --clock --json` (a child process): the
     median current shader clock over the XCDs, its range, whether it is
@@ -836,6 +896,10 @@ def main():
 
     if args.k_sweep:
         out["f16_k_sweep"] = f16_k_sweep(dev, stream, 100)
+
+    # ---- the fp16 tile's slab work without the GEMM (load path against MFMAs)
+    if not args.no_f16:
+        out["slab_probe"] = slab_probe(dev, stream)
 
     # ---- SGEMM 512^3 and the ragged full-form workloads -------------------------
     if not args.no_extra:

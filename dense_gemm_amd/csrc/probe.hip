@@ -1,5 +1,7 @@
 // Control probes of the GEMM measurements (libdense_gemm_probe.so): the
-// matrix-core peak with the shader clock under load, and a plain device copy.
+// matrix-core peak with the shader clock under load, a plain device copy, and
+// the per-slab work of the fp16 GEMM tile without the GEMM (direct loads and
+// MFMAs apart and together).
 // "Metal GEMM Kernels for LoRA Training on Apple Silicon", section 9: figures
 // are trusted only while a control benchmark stays within 10% of its
 // reference.  These kernels have exactly known costs, so they serve as that
@@ -15,6 +17,7 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 thread_local int g_last_hip_error = 0;
 
@@ -74,6 +77,150 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const i32x4 *src, i32x4 
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// The per-slab work of the 128x128 fp16 GEMM tile (two K groups of four
+// waves, four 32 KB LDS stages, one workgroup per CU), without its data
+// flow: each iteration is one slab.  It starts as a GEMM slab does (wait
+// until this wave has at most two slabs' loads in flight, one with
+// DGP_SLAB_DEPTH1, then a barrier); then each wave does the parts MODE names
+// (DGP_SLAB_* bits):
+//   LOADS  4 direct loads of 1 KB (buffer_load_dwordx4 ... lds, 16 bytes per
+//          lane), 32 KB per workgroup: a window of 256 rows x 128 bytes of
+//          `src`, seen as rows of `pitch` bytes (pitch 128: contiguous).
+//          Workgroup ids are dealt to the 8 XCDs in turn; the workgroups of
+//          one XCD share `windows` groups of 256 rows, the XCDs take
+//          different groups, and slab i reads column i % (pitch / 128) of
+//          its group, moving on to the next groups when the columns wrap,
+//          as a GEMM tile walks K along its A and B panels;
+//   MFMA   8 v_mfma_f32_32x32x16_f16 (16 per SIMD: the slab's matrix-core
+//          work), on 2 x 2 blocks of two 16-deep k steps;
+//   READS  8 fragment reads of 1 KB (ds_read_b128, 16 bytes per lane,
+//          conflict-free), 64 KB per workgroup, from the stage loaded two
+//          slabs earlier; with MFMA they are the next slab's operands, read
+//          while this slab's MFMAs run, as the GEMM reads them.
+// A load goes before every second MFMA step and a read before every one, in
+// that order (pinned with sched_barrier).  Without READS the MFMAs take
+// register operands; without MFMA the reads feed a sum.  The first wave
+// stamps the loop with s_memtime.
+template <int MODE>
+__global__ __launch_bounds__(512) void slab_probe_kernel(const char *src, uint32_t src_bytes, int iters,
+                                                        int windows, uint32_t pitch, float *sink,
+                                                        uint64_t *clocks)
+{
+    constexpr bool LOADS = (MODE & DGP_SLAB_LOADS) != 0;
+    constexpr bool MFMA = (MODE & DGP_SLAB_MFMA) != 0;
+    constexpr bool READS = (MODE & DGP_SLAB_READS) != 0;
+    constexpr bool DEPTH1 = (MODE & DGP_SLAB_DEPTH1) != 0;
+    typedef __attribute__((address_space(3))) f16x8 lds_f16x8_t;
+    __shared__ __attribute__((aligned(1024))) char lds_raw[4 * 32768];
+    lds_char_t *lds = (lds_char_t *)lds_raw;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // every LDS byte defined before any read (256 bytes per thread)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (_Float16)(0.001f * (float)((tid + i + e) & 63));
+        *(lds_f16x8_t *)(lds + (i * 512 + tid) * 16) = v;
+    }
+    __syncthreads();
+    // buffer resource over [src, src + src_bytes): reads past it return zero
+    const uint64_t b = (uint64_t)(uintptr_t)src;
+    i32x4 rsrc;
+    rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    rsrc[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff);
+    rsrc[2] = (int)src_bytes;
+    rsrc[3] = 0x00020000;
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    // two fragment sets: a slab's MFMAs take one while its reads fill the other
+    f16x8 fa[8], fb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            fa[i][e] = (_Float16)(lane * 0.001f + (i + e) * 0.01f - 0.05f);
+            fb[i][e] = fa[i][e];
+        }
+    i32x4 rsum = {0, 0, 0, 0};
+    const uint32_t group_bytes = 256u * pitch;
+    const uint32_t ngroups = src_bytes / group_bytes;    // groups of 256 rows src holds
+    const uint32_t ncols = pitch / 128u;                 // 128-byte columns of a row
+    const uint32_t gstep = (8u * (uint32_t)windows) % ngroups;   // groups the XCDs move on by
+    // this workgroup's group and column at slab 0
+    uint32_t grp = __builtin_amdgcn_readfirstlane(
+        (int)(((blockIdx.x & 7u) * (uint32_t)windows + (blockIdx.x >> 3) % (uint32_t)windows) % ngroups));
+    uint32_t col = 0;
+    // lane's byte in a 1 KB piece: row lane / 8 of the piece's 8, 16 bytes of 128
+    const uint32_t lane_off = (uint32_t)(lane >> 3) * pitch + (uint32_t)(lane & 7) * 16u;
+    auto slab = [&](int it, f16x8 (&use)[8], f16x8 (&fill)[8]) {
+        if constexpr (LOADS) {
+            // vmcnt <= 8: this wave's loads of three slabs ago have landed
+            // (vmcnt <= 4: of two slabs ago)
+            if constexpr (DEPTH1) __builtin_amdgcn_s_waitcnt((4 & 15) | (7 << 4) | (15 << 8));
+            else __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+        }
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        const int stage = (it & 3) * 32768;
+        const int rstage = ((it + 2) & 3) * 32768;      // loaded two slabs ago
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            if constexpr (LOADS) {
+                if (m % 2 == 0) {
+                    const int slot = (m / 2) * 8 + wave;          // 1 KB piece of the 32 KB slab
+                    const unsigned dst = (unsigned)(uintptr_t)(lds + stage + slot * 1024);
+                    const uint32_t voff = grp * group_bytes + (uint32_t)slot * 8u * pitch + col * 128u + lane_off;
+                    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                                 :
+                                 : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                                 : "memory");
+                }
+            }
+            if constexpr (READS) {
+                const int piece = (wave * 8 + m) & 31;        // 1 KB piece of the 32 KB stage
+                fill[m] = *(const lds_f16x8_t *)(lds + rstage + piece * 1024 + lane * 16);
+            }
+            if constexpr (MFMA) {
+                // k step t = m / 4, block (i, j) = ((m / 2) % 2, m % 2)
+                const int t = m / 4, i = (m / 2) % 2, j = m % 2;
+                acc[2 * i + j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(use[2 * t + i], use[4 + 2 * t + j],
+                                                                        acc[2 * i + j], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);             // keep the order as written
+        }
+        if constexpr (READS && !MFMA) {
+            // every byte read feeds the result (else the reads would narrow)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rsum ^= __builtin_bit_cast(i32x4, fill[i]);
+        }
+        if (++col == ncols) {
+            col = 0;
+            grp = grp + gstep >= ngroups ? grp + gstep - ngroups : grp + gstep;
+        }
+    };
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    int it = 0;
+    for (; it + 1 < iters; it += 2) {
+        slab(it, fa, fb);
+        slab(it + 1, fb, fa);
+    }
+    if (it < iters) slab(it, fa, fb);
+    if constexpr (LOADS) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));    // vmcnt(0)
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    float s = (float)(rsum[0] ^ rsum[1] ^ rsum[2] ^ rsum[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += acc[i][r];
+    sink[(int64_t)blockIdx.x * 512 + tid] = s;
+    if (tid == 0) clocks[blockIdx.x] = t1 - t0;
+}
+
 int hip_status(hipError_t e)
 {
     if (e == hipSuccess) return 0;
@@ -119,6 +266,44 @@ int dgp_copy(const void *src, void *dst, int64_t bytes, void *stream)
     if (blocks > 256 * 32) blocks = 256 * 32;
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream,
                        (const i32x4 *)src, (i32x4 *)dst, n16);
+    return hip_status(hipGetLastError());
+}
+
+int dgp_slab_probe(int mode, int64_t workgroups, int32_t iters, int32_t windows, int32_t pitch,
+                   const void *src, int64_t src_bytes, float *sink, uint64_t *clocks, void *stream)
+{
+    if (mode < 1 || mode > 15 || (mode & 7) == 0) return -1;
+    if (workgroups < 1 || workgroups > 65536) return -2;
+    if (iters < 1 || iters > (1 << 20)) return -3;
+    if (windows < 1 || windows > 32) return -4;
+    if (pitch < 128 || pitch > 65536 || pitch % 128 != 0) return -5;
+    if (!src || ((uintptr_t)src & 15)) return -6;
+    if (src_bytes < 256 * (int64_t)pitch || src_bytes % (256 * (int64_t)pitch) != 0 ||
+        src_bytes >= ((int64_t)1 << 31))
+        return -7;
+    if (!sink) return -8;
+    if (!clocks) return -9;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((unsigned)workgroups), block(512);
+    const char *p = (const char *)src;
+    const uint32_t nb = (uint32_t)src_bytes;
+    switch (mode) {
+    case 1: hipLaunchKernelGGL(slab_probe_kernel<1>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 2: hipLaunchKernelGGL(slab_probe_kernel<2>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 3: hipLaunchKernelGGL(slab_probe_kernel<3>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 4: hipLaunchKernelGGL(slab_probe_kernel<4>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 5: hipLaunchKernelGGL(slab_probe_kernel<5>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 6: hipLaunchKernelGGL(slab_probe_kernel<6>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 7: hipLaunchKernelGGL(slab_probe_kernel<7>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 8: hipLaunchKernelGGL(slab_probe_kernel<8>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 9: hipLaunchKernelGGL(slab_probe_kernel<9>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 10: hipLaunchKernelGGL(slab_probe_kernel<10>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 11: hipLaunchKernelGGL(slab_probe_kernel<11>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 12: hipLaunchKernelGGL(slab_probe_kernel<12>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 13: hipLaunchKernelGGL(slab_probe_kernel<13>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    case 14: hipLaunchKernelGGL(slab_probe_kernel<14>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    default: hipLaunchKernelGGL(slab_probe_kernel<15>, grid, block, 0, s, p, nb, (int)iters, (int)windows, (uint32_t)pitch, sink, clocks); break;
+    }
     return hip_status(hipGetLastError());
 }
 

@@ -13,6 +13,7 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python dense_gemm_amd/build.py`")
 
 DGP_MFMA_F32, DGP_MFMA_F16 = 0, 1
+DGP_SLAB_LOADS, DGP_SLAB_MFMA, DGP_SLAB_READS, DGP_SLAB_DEPTH1 = 1, 2, 4, 8
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp, _ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
@@ -22,12 +23,15 @@ _lib.dgp_mfma_flops.argtypes = [_ci, _i64, _i32]
 _lib.dgp_mfma_flops.restype = ctypes.c_double
 _lib.dgp_copy.argtypes = [_vp, _vp, _i64, _vp]
 _lib.dgp_copy.restype = _ci
+_lib.dgp_slab_probe.argtypes = [_ci, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _vp]
+_lib.dgp_slab_probe.restype = _ci
 _lib.dgp_wall_clock_khz.argtypes = []
 _lib.dgp_wall_clock_khz.restype = _ci
 _lib.dgp_last_hip_error.argtypes = []
 _lib.dgp_last_hip_error.restype = _ci
 
-EXPORTED = ["dgp_mfma_peak", "dgp_mfma_flops", "dgp_copy", "dgp_wall_clock_khz", "dgp_last_hip_error"]
+EXPORTED = ["dgp_mfma_peak", "dgp_mfma_flops", "dgp_copy", "dgp_slab_probe", "dgp_wall_clock_khz",
+            "dgp_last_hip_error"]
 
 
 def dgp_mfma_peak(kind, workgroups, iters, sink, clocks, stream):
@@ -40,6 +44,10 @@ def dgp_mfma_flops(kind, workgroups, iters):
 
 def dgp_copy(src, dst, nbytes, stream):
     return _lib.dgp_copy(src, dst, nbytes, stream)
+
+
+def dgp_slab_probe(mode, workgroups, iters, windows, pitch, src, src_bytes, sink, clocks, stream):
+    return _lib.dgp_slab_probe(mode, workgroups, iters, windows, pitch, src, src_bytes, sink, clocks, stream)
 
 
 def dgp_wall_clock_khz():

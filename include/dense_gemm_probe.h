@@ -12,7 +12,10 @@
  *   dgp_mfma_peak  back-to-back independent matrix-core instructions (no
  *                  memory traffic): sustained MFMA rate of the part, and the
  *                  shader clock while it runs;
- *   dgp_copy       a plain device copy: sustained HBM read + write rate.
+ *   dgp_copy       a plain device copy: sustained HBM read + write rate;
+ *   dgp_slab_probe the per-slab work of the fp16 GEMM's 128x128 tile (direct
+ *                  loads into LDS, fragment reads from LDS, MFMAs) in any
+ *                  combination, which separates the costs of the parts.
  *
  * Every function enqueues on `stream` (a hipStream_t, NULL for the default
  * stream), returns after enqueueing, and allocates nothing.  Buffers are
@@ -63,6 +66,49 @@ double dgp_mfma_flops(int kind, int64_t workgroups, int32_t iters);
  * multiple of 16.  The ranges must not overlap.
  */
 int dgp_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+enum {                  /* parts of a slab, combined with | */
+    DGP_SLAB_LOADS = 1, /* each wave: 4 direct loads of 1 KB into LDS */
+    DGP_SLAB_MFMA = 2,  /* each wave: 8 v_mfma_f32_32x32x16_f16 */
+    DGP_SLAB_READS = 4, /* each wave: 8 fragment reads of 1 KB (ds_read_b128) */
+    DGP_SLAB_DEPTH1 = 8 /* at each slab's start at most one slab of this wave's
+                           loads in flight (else two) */
+};
+
+/*
+ * Slab probe.  Launches `workgroups` workgroups of 512 threads (8 waves, 128
+ * KB of LDS: one per compute unit) that each run `iters` slabs of the fp16
+ * GEMM's 128x128 tile without its data flow: per slab a wait until at most
+ * two slabs' loads are in flight (one with DGP_SLAB_DEPTH1) and a barrier,
+ * then the parts `mode` names (a | of DGP_SLAB_* with at least one of
+ * LOADS, MFMA, READS): one load before every second MFMA step and one
+ * fragment read before every step, as the GEMM spreads them.
+ *
+ * The loads (buffer_load_dwordx4 ... lds) see src as rows of `pitch` bytes
+ * in groups of 256 rows.  Each slab a workgroup loads one 128-byte column of
+ * its group (32 KB), the next column the next slab, as a GEMM tile walks K
+ * along its A and B panels (pitch = the operands' row stride).  Workgroup
+ * ids are dealt to the 8 XCDs in turn: the workgroups of one XCD share
+ * `windows` groups, the XCDs take different groups, and when the columns
+ * wrap every workgroup moves on to groups not used before (modulo the groups
+ * src holds).  A src that fits L2 stays resident there; a larger one is
+ * fetched from the memory side as a GEMM's panels are.  The reads take the
+ * stage loaded two slabs earlier and, with MFMA, are the next slab's
+ * operands.
+ *   windows 1 .. 32
+ *   pitch   128 .. 65536, a multiple of 128 (128: contiguous windows)
+ *   src     device, src_bytes readable bytes, 16-byte aligned; src_bytes a
+ *           positive multiple of 256 * pitch, below 2^31
+ *   sink    device, workgroups * 512 floats, written
+ *   clocks  device, workgroups uint64 values, written: the shader-clock
+ *           ticks (s_memtime) the first wave of each workgroup spent in the
+ *           loop
+ * Errors: -1 mode invalid, -2 workgroups outside [1, 65536], -3 iters
+ * outside [1, 1 << 20], -4 windows outside [1, 32], -5 pitch invalid, -6 src
+ * null or not 16-byte aligned, -7 src_bytes invalid, -8 / -9 null buffers.
+ */
+int dgp_slab_probe(int mode, int64_t workgroups, int32_t iters, int32_t windows, int32_t pitch,
+                   const void *src, int64_t src_bytes, float *sink, uint64_t *clocks, void *stream);
 
 /* Frequency of the s_memrealtime counter of the current device, kHz (0 if unknown). */
 int dgp_wall_clock_khz(void);

@@ -75,6 +75,35 @@ def test_copy_invalid_arguments():
     assert pr.dgp_copy(16, 32, 0, None) == 0              # empty: nothing enqueued
 
 
+@pytest.mark.parametrize("args,code", [
+    ((0, 4, 10, 1, 128, 16, 32768), -1),
+    ((8, 4, 10, 1, 128, 16, 32768), -1),                      # depth alone: no part
+    ((16, 4, 10, 1, 128, 16, 32768), -1),
+    ((pr.DGP_SLAB_MFMA, 0, 10, 1, 128, 16, 32768), -2),
+    ((pr.DGP_SLAB_MFMA, 65537, 10, 1, 128, 16, 32768), -2),
+    ((pr.DGP_SLAB_LOADS, 4, 0, 1, 128, 16, 32768), -3),
+    ((pr.DGP_SLAB_LOADS, 4, (1 << 20) + 1, 1, 128, 16, 32768), -3),
+    ((pr.DGP_SLAB_LOADS, 4, 10, 0, 128, 16, 32768), -4),
+    ((pr.DGP_SLAB_LOADS, 4, 10, 33, 128, 16, 32768), -4),
+    ((pr.DGP_SLAB_LOADS, 4, 10, 1, 64, 16, 32768), -5),
+    ((pr.DGP_SLAB_LOADS, 4, 10, 1, 192, 16, 256 * 192), -5),    # not a multiple of 128
+    ((pr.DGP_SLAB_LOADS, 4, 10, 1, 65536 + 128, 16, 1 << 25), -5),
+    ((pr.DGP_SLAB_READS, 4, 10, 1, 128, None, 32768), -6),
+    ((pr.DGP_SLAB_READS, 4, 10, 1, 128, 8, 32768), -6),        # not 16-byte aligned
+    ((pr.DGP_SLAB_MFMA, 4, 10, 1, 128, 16, 0), -7),
+    ((pr.DGP_SLAB_MFMA, 4, 10, 1, 128, 16, 32768 + 16), -7),  # not whole groups of 256 rows
+    ((pr.DGP_SLAB_MFMA, 4, 10, 1, 4096, 16, 1 << 19), -7),    # less than one group at this pitch
+    ((pr.DGP_SLAB_MFMA, 4, 10, 1, 128, 16, 1 << 31), -7),
+])
+def test_slab_probe_invalid_arguments(args, code):
+    assert pr.dgp_slab_probe(*args, 16, 16, None) == code
+
+
+def test_slab_probe_null_buffers():
+    assert pr.dgp_slab_probe(pr.DGP_SLAB_MFMA, 4, 10, 1, 128, 16, 32768, None, 16, None) == -8
+    assert pr.dgp_slab_probe(pr.DGP_SLAB_MFMA, 4, 10, 1, 128, 16, 32768, 16, None, None) == -9
+
+
 @pytest.mark.gpu
 def test_copy_is_exact():
     import torch
@@ -112,3 +141,62 @@ def test_mfma_probe_runs(kind):
     assert khz > 0
     mhz = (c[:, 0].double() / c[:, 1].double()).median().item() * khz / 1e3
     assert 500 < mhz < 3000, mhz                           # a shader clock, in MHz
+
+
+@pytest.mark.gpu
+def test_slab_probe_runs():
+    """Every combination of the slab probe's parts on one workgroup per CU:
+    every workgroup reports its cycles, a slab with MFMAs takes at least
+    their 512 cycles per SIMD (less would mean the instructions were not
+    run), and a combination takes at least as long as each of its parts."""
+    import statistics
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    slabs = 500
+    src = torch.ones(1 << 18, dtype=torch.float32, device=dev)             # 1 MiB
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs, dtype=torch.int64, device=dev)
+    s = torch.cuda.current_stream()
+    cyc = {}
+    for mode in list(range(1, 8)) + [pr.DGP_SLAB_DEPTH1 | m for m in (1, 3, 5, 7)]:
+        print(f"slab probe mode={mode} wgs={wgs} slabs={slabs}", flush=True)
+        assert pr.dgp_slab_probe(mode, wgs, slabs, 1, 128, src.data_ptr(), src.numel() * 4, sink.data_ptr(),
+                                 clocks.data_ptr(), s.cuda_stream) == 0
+        torch.cuda.synchronize()
+        c = clocks.cpu().tolist()
+        assert all(x > 0 for x in c)
+        cyc[mode] = statistics.median(c) / slabs
+    for mode in cyc:
+        if mode & pr.DGP_SLAB_MFMA:
+            assert cyc[mode] >= 0.95 * 512, cyc
+        for part in (pr.DGP_SLAB_LOADS, pr.DGP_SLAB_MFMA, pr.DGP_SLAB_READS):
+            if mode & part and mode & 7 != part:
+                assert cyc[mode] >= 0.9 * cyc[part], (mode, part, cyc)
+
+
+@pytest.mark.gpu
+def test_slab_probe_groups_wrap():
+    """Group counts that do not divide the source's groups, more groups than
+    it holds, and pitches from contiguous to 64 KB rows: every load stays
+    inside the source (the group index wraps) and the probe completes."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs, dtype=torch.int64, device=dev)
+    s = torch.cuda.current_stream()
+    for pitch, groups in ((128, 5), (4096, 3), (65536, 1)):
+        src = torch.ones(groups * 256 * pitch // 4, dtype=torch.float32, device=dev)
+        for windows in (1, 3, 5, 7, 32):
+            print(f"slab probe pitch={pitch} groups={groups} windows={windows}", flush=True)
+            assert pr.dgp_slab_probe(pr.DGP_SLAB_LOADS | pr.DGP_SLAB_READS | pr.DGP_SLAB_MFMA, wgs, 37, windows,
+                                     pitch, src.data_ptr(), src.numel() * 4, sink.data_ptr(), clocks.data_ptr(),
+                                     s.cuda_stream) == 0
+            torch.cuda.synchronize()
+            assert all(x > 0 for x in clocks.cpu().tolist())
+        del src
