@@ -185,7 +185,9 @@ def cold_launches(fn, stream, n, scrub):
 def control_probes(dev, stream):
     """The control benchmarks (libdense_gemm_probe.so): matrix-core peak of the
     fp32 and fp16 instructions the GEMMs use, with the shader clock while they
-    run, and the plain-copy HBM rate; each against its reference."""
+    run, and the plain-copy HBM rate; each against its reference.  Beside
+    them, not gated: the fp16 matrix-core rate on pseudo-random operands that
+    change every instruction, at the clock the part holds under that load."""
     import statistics
     import torch
 
@@ -197,7 +199,8 @@ def control_probes(dev, stream):
     clocks = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
     khz = pr.dgp_wall_clock_khz()
     res = {}
-    for name, kind, iters in (("mfma_f32", pr.DGP_MFMA_F32, 8000), ("mfma_f16", pr.DGP_MFMA_F16, 16000)):
+    for name, kind, iters in (("mfma_f32", pr.DGP_MFMA_F32, 8000), ("mfma_f16", pr.DGP_MFMA_F16, 16000),
+                              ("mfma_f16_random", pr.DGP_MFMA_F16_RANDOM, 16000)):
         def f(kind=kind, iters=iters):
             rc = pr.dgp_mfma_peak(kind, wgs, iters, sink.data_ptr(), clocks.data_ptr(), sptr)
             if rc != 0:
@@ -228,6 +231,10 @@ def control_probes(dev, stream):
           and gbs >= (1 - CONTROL_TOL) * REF_COPY_GBS)
     return {"mfma_f32_tflops": res["mfma_f32"]["tflops"], "mfma_f32_clock_mhz": res["mfma_f32"]["clock_mhz"],
             "mfma_f16_tflops": res["mfma_f16"]["tflops"], "mfma_f16_clock_mhz": res["mfma_f16"]["clock_mhz"],
+            # not gated: the matrix cores on operands that change every
+            # instruction, as in a GEMM on random data (power sets the clock)
+            "mfma_f16_random_tflops": res["mfma_f16_random"]["tflops"],
+            "mfma_f16_random_clock_mhz": res["mfma_f16_random"]["clock_mhz"],
             "copy_gbs": round(gbs, 1), "copy_frac_of_hbm_peak": round(gbs / HBM_PEAK, 3),
             "references": {"mfma_f32_tflops": REF_MFMA_F32, "mfma_f16_tflops": REF_MFMA_F16,
                            "copy_gbs": REF_COPY_GBS, "tolerance": CONTROL_TOL},
@@ -644,9 +651,9 @@ def slab_probe(dev, stream, slabs=2000):
     """The slab probe (libdense_gemm_probe.so, dgp_slab_probe): one workgroup
     per CU doing the per-slab work of the fp16 2048^3 tile without its data
     flow -- per SIMD and slab 8 KB of direct loads into LDS, 16 KB of
-    fragment reads from LDS and 16 MFMAs.  Shader cycles per slab: the median
-    over the workgroups of the first wave's s_memtime span, from the second
-    of two launches.
+    fragment reads from LDS and 16 MFMAs.  Per slab: shader cycles and
+    nanoseconds, the medians over the workgroups of the first wave's
+    s_memtime and s_memrealtime spans, from the second of two launches.
       l2        each combination of the parts, loading contiguous 32 KB
                 windows of a 1 MiB source that stays in L2;
       patterns  loads alone and all three parts for load patterns between
@@ -665,7 +672,8 @@ def slab_probe(dev, stream, slabs=2000):
     sptr = stream.cuda_stream
     wgs = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
-    clocks = torch.zeros(wgs, dtype=torch.int64, device=dev)
+    clocks = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
+    khz = pr.dgp_wall_clock_khz()
     L, M, R = pr.DGP_SLAB_LOADS, pr.DGP_SLAB_MFMA, pr.DGP_SLAB_READS
 
     def run(mode, windows, pitch, src):
@@ -675,7 +683,10 @@ def slab_probe(dev, stream, slabs=2000):
             if rc != 0:
                 raise RuntimeError(f"dgp_slab_probe failed ({rc}, hip {pr.dgp_last_hip_error()})")
         torch.cuda.synchronize()
-        return round(statistics.median(int(x) for x in clocks.cpu().tolist()) / slabs, 1)
+        c = clocks.view(wgs, 2).cpu().tolist()
+        cyc = statistics.median(x for x, _ in c) / slabs
+        ns = statistics.median(y for _, y in c) / slabs / khz * 1e6 if khz > 0 else None
+        return {"cycles": round(cyc, 1), "ns": None if ns is None else round(ns, 1)}
 
     mib = 1 << 18                                                       # floats per MiB
     small = torch.ones(mib, dtype=torch.float32, device=dev)
@@ -696,8 +707,25 @@ def slab_probe(dev, stream, slabs=2000):
         patterns[name] = {"loads": run(L, windows, pitch, src), "loads+reads+mfma": run(L | R | M, windows, pitch, src),
                           "loads+reads+mfma, one slab in flight": run(L | R | M | D, windows, pitch, src)}
         del src
+    # the GEMM tiles' own loads: A and B panels of a 16 x 16 tile grid, the
+    # nt operands of 2048 x 2048 x K, tiles dealt to XCDs in the library's
+    # order, 1 .. 16 tile rows per group (the 128 x 128 kernel takes 4)
+    gemm = {}
+    T = int(round(wgs ** 0.5))
+    if T * T == wgs:
+        P = pr.DGP_SLAB_PANELS
+        for K in (2048, 8192):
+            src = torch.ones(2 * T * 128 * 2 * K // 4, dtype=torch.float32, device=dev)
+            for gm in (1, 2, 4, 8, 16):
+                if gm <= T:
+                    gemm[f"K={K}, {gm} tile rows per group"] = run(L | R | M | P, gm, 2 * K, src)
+            # the lanes of a row fetching its chunks in the GEMM's XOR order
+            gemm[f"K={K}, 4 tile rows per group, swizzled lanes"] = run(L | R | M | P | pr.DGP_SLAB_SWIZZLE, 4,
+                                                                       2 * K, src)
+            del src
     return {"workgroups": wgs, "slabs": slabs, "mfma_cycles_per_slab_at_peak": 16 * 32,
-            "cycles_per_slab_l2": l2, "cycles_per_slab_by_load_pattern": patterns}
+            "cycles_per_slab_l2": l2, "cycles_per_slab_by_load_pattern": patterns,
+            "gemm_tile_panels": gemm}
 
 
 def smi_clocks(index=0):
@@ -872,6 +900,9 @@ def main():
             ach = tflops(S, S, S, t16)
             res[name] = {"tflops": round(ach, 2), "frac": round(ach / PEAK_F16, 4),
                          "frac_of_probe_peak": round(ach / control["mfma_f16_tflops"], 4),
+                         # against the matrix cores alone on operands that change every
+                         # instruction (the clock the part holds on such data)
+                         "frac_of_random_operand_probe": round(ach / control["mfma_f16_random_tflops"], 4),
                          "kernel_us": round(t16 * 1e6, 2), "kernel": dg.dg_kernel_name(k16),
                          "traffic": measured_traffic(k16, ta, tb, S, S),
                          "algorithmic_bytes": 3 * S * S * 2,

@@ -12,8 +12,8 @@ LIB_PATH = os.path.join(_HERE, "libdense_gemm_probe.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python dense_gemm_amd/build.py`")
 
-DGP_MFMA_F32, DGP_MFMA_F16 = 0, 1
-DGP_SLAB_LOADS, DGP_SLAB_MFMA, DGP_SLAB_READS, DGP_SLAB_DEPTH1 = 1, 2, 4, 8
+DGP_MFMA_F32, DGP_MFMA_F16, DGP_MFMA_F16_RANDOM = 0, 1, 2
+DGP_SLAB_LOADS, DGP_SLAB_MFMA, DGP_SLAB_READS, DGP_SLAB_DEPTH1, DGP_SLAB_PANELS, DGP_SLAB_SWIZZLE = 1, 2, 4, 8, 16, 32
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp, _ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int

@@ -36,8 +36,10 @@ extern "C" {
 #endif
 
 enum {
-    DGP_MFMA_F32 = 0,   /* v_mfma_f32_32x32x2_f32: 4096 flops per wave instruction */
-    DGP_MFMA_F16 = 1    /* v_mfma_f32_32x32x16_f16: 32768 flops per wave instruction */
+    DGP_MFMA_F32 = 0,        /* v_mfma_f32_32x32x2_f32: 4096 flops per wave instruction */
+    DGP_MFMA_F16 = 1,        /* v_mfma_f32_32x32x16_f16: 32768 flops per wave instruction */
+    DGP_MFMA_F16_RANDOM = 2  /* the same on pseudo-random operands in [-1, 1) that change
+                                every instruction (the matrix cores' power on real data) */
 };
 
 /*
@@ -71,8 +73,10 @@ enum {                  /* parts of a slab, combined with | */
     DGP_SLAB_LOADS = 1, /* each wave: 4 direct loads of 1 KB into LDS */
     DGP_SLAB_MFMA = 2,  /* each wave: 8 v_mfma_f32_32x32x16_f16 */
     DGP_SLAB_READS = 4, /* each wave: 8 fragment reads of 1 KB (ds_read_b128) */
-    DGP_SLAB_DEPTH1 = 8 /* at each slab's start at most one slab of this wave's
-                           loads in flight (else two) */
+    DGP_SLAB_DEPTH1 = 8, /* at each slab's start at most one slab of this wave's
+                            loads in flight (else two) */
+    DGP_SLAB_PANELS = 16, /* loads of a GEMM tile's A and B panels (see below) */
+    DGP_SLAB_SWIZZLE = 32 /* a row's chunks fetched in the fp16 GEMM's lane order */
 };
 
 /*
@@ -92,7 +96,17 @@ enum {                  /* parts of a slab, combined with | */
  * `windows` groups, the XCDs take different groups, and when the columns
  * wrap every workgroup moves on to groups not used before (modulo the groups
  * src holds).  A src that fits L2 stays resident there; a larger one is
- * fetched from the memory side as a GEMM's panels are.  The reads take the
+ * fetched from the memory side as a GEMM's panels are.  With
+ * DGP_SLAB_PANELS the loads are exactly those of a tile of the k-contiguous
+ * (nt) GEMM: src holds A and then B, T * 128 rows of `pitch` bytes each,
+ * workgroups must be T * T, and workgroup w loads the A and B panels of
+ * tile w in the order the GEMM kernels deal tiles to the XCDs, with
+ * `windows` (at most T) tile rows per group; one 128-byte column of each
+ * panel per slab, the columns wrapping at the end of the rows.  With
+ * DGP_SLAB_SWIZZLE the 8 lanes that load one 128-byte row take its 16-byte
+ * chunks in the XOR order of the fp16 GEMM's k-contiguous LDS layout (the
+ * lane at chunk slot p of row r: chunk p ^ ((r / 2) % 8), r counted within
+ * the 256-row window or the 128-row panel) instead of address order.  The reads take the
  * stage loaded two slabs earlier and, with MFMA, are the next slab's
  * operands.
  *   windows 1 .. 32
@@ -100,12 +114,14 @@ enum {                  /* parts of a slab, combined with | */
  *   src     device, src_bytes readable bytes, 16-byte aligned; src_bytes a
  *           positive multiple of 256 * pitch, below 2^31
  *   sink    device, workgroups * 512 floats, written
- *   clocks  device, workgroups uint64 values, written: the shader-clock
- *           ticks (s_memtime) the first wave of each workgroup spent in the
- *           loop
- * Errors: -1 mode invalid, -2 workgroups outside [1, 65536], -3 iters
- * outside [1, 1 << 20], -4 windows outside [1, 32], -5 pitch invalid, -6 src
- * null or not 16-byte aligned, -7 src_bytes invalid, -8 / -9 null buffers.
+ *   clocks  device, workgroups * 2 uint64 values, written: for each
+ *           workgroup, the shader-clock ticks (s_memtime) and the constant
+ *           wall-clock ticks (s_memrealtime, dgp_wall_clock_khz() per ms)
+ *           its first wave spent in the loop
+ * Errors: -1 mode invalid, -2 workgroups outside [1, 65536] (with PANELS:
+ * not T * T), -3 iters outside [1, 1 << 20], -4 windows outside [1, 32]
+ * (with PANELS: above T), -5 pitch invalid, -6 src null or not 16-byte
+ * aligned, -7 src_bytes invalid, -8 / -9 null buffers.
  */
 int dgp_slab_probe(int mode, int64_t workgroups, int32_t iters, int32_t windows, int32_t pitch,
                    const void *src, int64_t src_bytes, float *sink, uint64_t *clocks, void *stream);

@@ -46,6 +46,7 @@ def test_flop_count_closed_form():
     # 8 MFMAs per round, 4 waves per workgroup; 2*32*32*2 and 2*32*32*16 flops each
     assert pr.dgp_mfma_flops(pr.DGP_MFMA_F32, 512, 1000) == 512 * 4 * 1000 * 8 * 4096
     assert pr.dgp_mfma_flops(pr.DGP_MFMA_F16, 3, 7) == 3 * 4 * 7 * 8 * 32768
+    assert pr.dgp_mfma_flops(pr.DGP_MFMA_F16_RANDOM, 3, 7) == 3 * 4 * 7 * 8 * 32768
     assert pr.dgp_mfma_flops(9, 512, 1000) == 0.0
 
 
@@ -78,7 +79,8 @@ def test_copy_invalid_arguments():
 @pytest.mark.parametrize("args,code", [
     ((0, 4, 10, 1, 128, 16, 32768), -1),
     ((8, 4, 10, 1, 128, 16, 32768), -1),                      # depth alone: no part
-    ((16, 4, 10, 1, 128, 16, 32768), -1),
+    ((64, 4, 10, 1, 128, 16, 32768), -1),
+    ((pr.DGP_SLAB_SWIZZLE, 4, 10, 1, 128, 16, 32768), -1),    # no part
     ((pr.DGP_SLAB_MFMA, 0, 10, 1, 128, 16, 32768), -2),
     ((pr.DGP_SLAB_MFMA, 65537, 10, 1, 128, 16, 32768), -2),
     ((pr.DGP_SLAB_LOADS, 4, 0, 1, 128, 16, 32768), -3),
@@ -94,6 +96,9 @@ def test_copy_invalid_arguments():
     ((pr.DGP_SLAB_MFMA, 4, 10, 1, 128, 16, 32768 + 16), -7),  # not whole groups of 256 rows
     ((pr.DGP_SLAB_MFMA, 4, 10, 1, 4096, 16, 1 << 19), -7),    # less than one group at this pitch
     ((pr.DGP_SLAB_MFMA, 4, 10, 1, 128, 16, 1 << 31), -7),
+    # a GEMM tile grid: T x T workgroups for src = 2 * T * 128 rows, at most T rows per group
+    ((pr.DGP_SLAB_LOADS | pr.DGP_SLAB_PANELS, 15, 10, 1, 128, 16, 4 * 128 * 128), -2),
+    ((pr.DGP_SLAB_LOADS | pr.DGP_SLAB_PANELS, 4, 10, 3, 128, 16, 4 * 128 * 128), -4),
 ])
 def test_slab_probe_invalid_arguments(args, code):
     assert pr.dgp_slab_probe(*args, 16, 16, None) == code
@@ -121,7 +126,7 @@ def test_copy_is_exact():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kind", [pr.DGP_MFMA_F32, pr.DGP_MFMA_F16])
+@pytest.mark.parametrize("kind", [pr.DGP_MFMA_F32, pr.DGP_MFMA_F16, pr.DGP_MFMA_F16_RANDOM])
 def test_mfma_probe_runs(kind):
     import torch
     if not torch.cuda.is_available():
@@ -158,7 +163,7 @@ def test_slab_probe_runs():
     slabs = 500
     src = torch.ones(1 << 18, dtype=torch.float32, device=dev)             # 1 MiB
     sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
-    clocks = torch.zeros(wgs, dtype=torch.int64, device=dev)
+    clocks = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
     s = torch.cuda.current_stream()
     cyc = {}
     for mode in list(range(1, 8)) + [pr.DGP_SLAB_DEPTH1 | m for m in (1, 3, 5, 7)]:
@@ -166,9 +171,11 @@ def test_slab_probe_runs():
         assert pr.dgp_slab_probe(mode, wgs, slabs, 1, 128, src.data_ptr(), src.numel() * 4, sink.data_ptr(),
                                  clocks.data_ptr(), s.cuda_stream) == 0
         torch.cuda.synchronize()
-        c = clocks.cpu().tolist()
-        assert all(x > 0 for x in c)
-        cyc[mode] = statistics.median(c) / slabs
+        c = clocks.view(wgs, 2).cpu().tolist()
+        assert all(x > 0 and y > 0 for x, y in c)
+        cyc[mode] = statistics.median(x for x, _ in c) / slabs
+        mhz = statistics.median(x / y for x, y in c) * pr.dgp_wall_clock_khz() / 1e3
+        assert 500 < mhz < 3000, (mode, mhz)                 # a shader clock, in MHz
     for mode in cyc:
         if mode & pr.DGP_SLAB_MFMA:
             assert cyc[mode] >= 0.95 * 512, cyc
@@ -188,7 +195,7 @@ def test_slab_probe_groups_wrap():
     dev = torch.device("cuda:0")
     wgs = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
-    clocks = torch.zeros(wgs, dtype=torch.int64, device=dev)
+    clocks = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
     s = torch.cuda.current_stream()
     for pitch, groups in ((128, 5), (4096, 3), (65536, 1)):
         src = torch.ones(groups * 256 * pitch // 4, dtype=torch.float32, device=dev)
@@ -199,4 +206,34 @@ def test_slab_probe_groups_wrap():
                                      s.cuda_stream) == 0
             torch.cuda.synchronize()
             assert all(x > 0 for x in clocks.cpu().tolist())
+        del src
+
+
+@pytest.mark.gpu
+def test_slab_probe_gemm_panels():
+    """The probe with a GEMM tile grid's panel loads (T x T workgroups, T =
+    16 for 256 CUs), at two row pitches and several tile rows per group:
+    completes, every workgroup reports."""
+    import math
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    T = math.isqrt(wgs)
+    if T * T != wgs:
+        pytest.skip("compute-unit count is not a square")
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
+    s = torch.cuda.current_stream()
+    for pitch in (4096, 128 * 3):
+        src = torch.ones(2 * T * 128 * pitch // 4, dtype=torch.float32, device=dev)
+        for gm in (1, 4, T):
+            print(f"slab probe panels T={T} pitch={pitch} group_m={gm}", flush=True)
+            for swz in (0, pr.DGP_SLAB_SWIZZLE):
+                mode = pr.DGP_SLAB_LOADS | pr.DGP_SLAB_READS | pr.DGP_SLAB_MFMA | pr.DGP_SLAB_PANELS | swz
+                assert pr.dgp_slab_probe(mode, wgs, 50, gm, pitch, src.data_ptr(), src.numel() * 4,
+                                         sink.data_ptr(), clocks.data_ptr(), s.cuda_stream) == 0
+                torch.cuda.synchronize()
+                assert all(x > 0 for x in clocks.cpu().tolist())
         del src
