@@ -709,7 +709,8 @@ def slab_probe(dev, stream, slabs=2000):
         del src
     # the GEMM tiles' own loads: A and B panels of a 16 x 16 tile grid, the
     # nt operands of 2048 x 2048 x K, tiles dealt to XCDs in the library's
-    # order, 1 .. 16 tile rows per group (the 128 x 128 kernel takes 4)
+    # order, 1 .. 16 tile rows per group (the 128 x 128 kernel takes 4); the
+    # source holds ones (half of the fp16 operands zero) unless stated
     gemm = {}
     T = int(round(wgs ** 0.5))
     if T * T == wgs:
@@ -720,8 +721,13 @@ def slab_probe(dev, stream, slabs=2000):
                 if gm <= T:
                     gemm[f"K={K}, {gm} tile rows per group"] = run(L | R | M | P, gm, 2 * K, src)
             # the lanes of a row fetching its chunks in the GEMM's XOR order
-            gemm[f"K={K}, 4 tile rows per group, swizzled lanes"] = run(L | R | M | P | pr.DGP_SLAB_SWIZZLE, 4,
-                                                                       2 * K, src)
+            Z = pr.DGP_SLAB_SWIZZLE
+            gemm[f"K={K}, 4 tile rows per group, swizzled lanes"] = run(L | R | M | P | Z, 4, 2 * K, src)
+            # the same over random fp16 operands (as the GEMM's), which the
+            # matrix cores multiply at a lower clock
+            g = torch.Generator(device=dev).manual_seed(6)
+            src.copy_((torch.randn(src.numel() * 2, device=dev, generator=g) / 8).half().view(torch.float32))
+            gemm[f"K={K}, 4 tile rows per group, swizzled lanes, random fp16"] = run(L | R | M | P | Z, 4, 2 * K, src)
             del src
     return {"workgroups": wgs, "slabs": slabs, "mfma_cycles_per_slab_at_peak": 16 * 32,
             "cycles_per_slab_l2": l2, "cycles_per_slab_by_load_pattern": patterns,
