@@ -99,6 +99,8 @@ const Family kFamilies[] = {
     {"f32_128x64_pipe4_dw_mfma32x32x2", DG_F32, 128, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 7},
     {"f32_64x64_pipe4_dw_mfma32x32x2", DG_F32, 64, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 8},
     {"f32_64x64_pipe3_k32_mfma32x32x2", DG_F32, 64, 64, 8, PIPE, dg::f32_pipe_launchers, 9},
+    {"f32_32x32_pipe3_k32_ksplit4_mfma32x32x2", DG_F32, 32, 32, 8, PIPE, dg::f32_pipe_launchers, 10},
+    {"f32_32x32_pipe4_k32_ksplit4_mfma32x32x2", DG_F32, 32, 32, 8, PIPE, dg::f32_pipe_launchers, 11},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -110,7 +112,8 @@ enum {
     K_F16_PIPE_256x256 = 22, K_BF16_PIPE_256x256 = 23, K_F32_PIPE_256x128_DW = 24,
     K_F32_PIPE_128_DW = 25, K_F16_PIPE_128_DW = 26, K_F16_PIPE_64_DW = 27, K_BF16_PIPE_128_DW = 28,
     K_BF16_PIPE_64_DW = 29, K_BF16_128 = 30, K_BF16_256 = 31, K_F32_PIPE_128x64 = 32,
-    K_F32_PIPE_64 = 33, K_F32_PIPE_128x64_DW = 34, K_F32_PIPE_64_DW = 35, K_F32_PIPE_64_K32 = 36
+    K_F32_PIPE_64 = 33, K_F32_PIPE_128x64_DW = 34, K_F32_PIPE_64_DW = 35, K_F32_PIPE_64_K32 = 36,
+    K_F32_PIPE_32_KG4 = 37, K_F32_PIPE_32_KG4_S4 = 38
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -315,6 +318,19 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
             // per CU but need two of three: there the 16-deep kernel stays
             // (2048^3 and 2048^2x1024 nt, tn, tt 3-19% slower on the 32-deep
             // one, 1792^2x2048 2-4%).
+            //
+            // Fewer 64x64 tiles than CUs: the 32x32 tile with four K groups,
+            // one wave per SIMD for each tile, so four times the tiles and
+            // every SIMD of their CUs at work.  Against the 64x64 32-deep
+            // kernel, one machine: 512^3 5.4-6.1 against 11.8-12.4 us (all
+            // four transpose pairs), 256^3 4.5 against 8.1, 768^3 14.2
+            // against 17.2, 512^2x2048 15.7 against 37.6, 512^2x8192 60
+            // against 138; even at 256 tiles (1024^3 21.7 against 21.8,
+            // 2048x512x512 13.1 against 13.3), 6% slower at 1024^2x4096.
+            // From K = 4096 with four stages: 512^2x8192 41.8-53.6 us against
+            // 48.9-62.8 with three (all four transpose pairs); at K up to
+            // 2048 the fourth stage cost 1-4% (512^3 tt 6.38 against 6.11).
+            if (pk == 3 && t64 < 256) return K >= 4096 ? K_F32_PIPE_32_KG4_S4 : K_F32_PIPE_32_KG4;
             if (pk == 3 && (t64 <= 768 || t64 > 1024)) return K_F32_PIPE_64_K32;
             return pipe16[pk];
         }

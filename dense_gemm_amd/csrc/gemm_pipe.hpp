@@ -337,6 +337,13 @@ struct PipeOperandS {
     // block row holds columns 0-31; the two half-waves (k rows HK apart)
     // then read different halves.
     static __device__ __forceinline__ int hsw(int r) { return (r >> HK_LOG) & 1; }
+    // A 32-wide m/n-contiguous tile has 128-byte k rows, one block wide: there
+    // the rows of the second half of the slab swap places in pairs (k row r
+    // sits at LDS row r ^ 1 when r >= HK), so that the two half-waves of a
+    // fragment read, HK rows apart, fall on rows of opposite parity and so on
+    // different halves of the 64 banks.
+    static constexpr bool NARROW = !KCONT && BMN == 32;
+    static __device__ __forceinline__ int krow(int r) { return NARROW ? r ^ ((r >> HK_LOG) & 1) : r; }
     static constexpr int BYTES = BMN * BK * 4;            // one stage
     static constexpr int SPAN = 64 * LB;                   // LDS bytes of one wave-wide load
     static constexpr int LOADS = BYTES / (NW * SPAN);      // loads per thread per slab
@@ -367,9 +374,9 @@ struct PipeOperandS {
                     row = row < ext ? row : ext - 1;
                     off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4) * 4);
                 } else {
-                    const int r = rbase + (lane / (ROW_BYTES / 16));  // k row
+                    const int r = krow(rbase + (lane / (ROW_BYTES / 16)));  // k row
                     const int p = lane % (ROW_BYTES / 16);            // physical 16-byte slot
-                    const int q = (p >> 3) ^ hsw(r);                  // logical 128-byte chunk
+                    const int q = NARROW ? 0 : (p >> 3) ^ hsw(r);     // logical 128-byte chunk
                     int col = mn0 + q * 32 + (p & 7) * 4;
                     col = col < ext ? col : ext - 4;
                     off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
@@ -384,10 +391,11 @@ struct PipeOperandS {
                     row = row < ext ? row : ext - 1;
                     off[i] = (uint32_t)(((int64_t)(row - mn0) * ld + c * 4 + e) * 4);
                 } else {
-                    const int q = (p >> 3) ^ hsw(r);
+                    const int k = krow(r);
+                    const int q = NARROW ? 0 : (p >> 3) ^ hsw(k);
                     int col = mn0 + q * 32 + (p & 7) * 4 + e;
                     col = col < ext ? col : ext - 1;
-                    off[i] = (uint32_t)(((int64_t)r * ld + (col - mn0)) * 4);
+                    off[i] = (uint32_t)(((int64_t)k * ld + (col - mn0)) * 4);
                 }
             }
         }
@@ -409,7 +417,7 @@ struct PipeOperandS {
                     const int c = (lane & (CH - 1)) ^ swz(r);
                     valid = krem - c * 4;
                 } else {
-                    const int r = (i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16));
+                    const int r = krow((i * NW + wave) * ROWS_PER_LOAD + (lane / (ROW_BYTES / 16)));
                     valid = r < krem ? 4 : 0;
                 }
                 f32x4 v;
@@ -428,7 +436,7 @@ struct PipeOperandS {
                 const int b = (i * NW + wave) * SPAN + lane * 4;
                 const int r = b / ROW_BYTES, w = b % ROW_BYTES;
                 const int p = w >> 4, e = (w >> 2) & 3;
-                const int k = KCONT ? (p ^ swz(r)) * 4 + e : r;   // this element's k
+                const int k = KCONT ? (p ^ swz(r)) * 4 + e : krow(r);   // this element's k
                 *(__attribute__((address_space(3))) float *)(lds + b) = k < krem ? *src : 0.f;
             }
         }
@@ -464,6 +472,13 @@ struct PipeOperandS {
             const int c = (h << (CH_LOG - 1)) + c2;
             const int p = c ^ swz(r);
             return *(const lds_f32x4_t *)(lds + r * ROW_BYTES + p * 16);
+        } else if constexpr (NARROW) {
+            // k row HK*h + 4*c2 + e sits at LDS row HK*h + ((4*c2 + e) ^ h)
+            const lds_char_t *base = lds + (h << HK_LOG) * ROW_BYTES + (lane & 31) * 4;
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = *(const lds_float_t *)(base + ((4 * c2 + e) ^ h) * ROW_BYTES);
+            return v;
         } else {
             const int q = (b0 >> 5) ^ h;   // hsw(k) == h for k = HK*h + ...
             const lds_char_t *base = lds + ((h << HK_LOG) + 4 * c2) * ROW_BYTES + q * 128 + (lane & 31) * 4;
@@ -476,6 +491,76 @@ struct PipeOperandS {
 };
 
 
+// The end of an fp32 kernel with K groups (one 32 x 32 block per wave).
+// Wave w = g*NWG + q (group g, sub-tile q) stages its partial block as fp32
+// [32][EPI_LD] in LDS slot w; after a barrier, wave w takes rows
+// 32/KSPLIT*g .. +32/KSPLIT-1 of sub-tile q, 8 rows per pass (lane l row
+// l/8 of the pass, columns 4*(l%8) .. +3), sums the KSPLIT partials in increasing group order,
+// and writes alpha*sum + beta*C + bias and the activation (fp32, 16-byte
+// stores where the row allows), or the raw sum to the split-K workspace.
+template <int KSPLIT, int NWG, int WAVES_N, int WM, int WN, int EPI_LD>
+__device__ __forceinline__ void fp32_groups_epilogue(const GemmParams &p, lds_char_t *smem, const f32x16 &acc,
+                                                     int wave, int lane, int m0, int n0, int split)
+{
+    typedef __attribute__((address_space(3))) float lds_float_t;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+    constexpr int SLOT = 32 * EPI_LD * 4;
+    constexpr int ROWS = 32 / KSPLIT;                // rows of the block per group, 8 per pass
+    lds_char_t *stg = smem + wave * SLOT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + (lane >> 5) * 4 + (r & 3);
+        *(lds_float_t *)(stg + (row * EPI_LD + (lane & 31)) * 4) = acc[r];
+    }
+    __syncthreads();
+    const int g = wave / NWG, q = wave % NWG;
+    const int lc = (lane & 7) * 4;
+    const int gcol = n0 + (q % WAVES_N) * WN + lc;
+#pragma unroll
+    for (int pass = 0; pass < ROWS / 8; ++pass) {
+        const int lr = ROWS * g + 8 * pass + (lane >> 3);
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gg = 0; gg < KSPLIT; ++gg) {
+            const f32x4 x = *(const lds_f32x4_t *)(smem + (gg * NWG + q) * SLOT + (lr * EPI_LD + lc) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += x[e];
+        }
+        const int grow = m0 + (q / WAVES_N) * WM + lr;
+        if (grow >= p.M) continue;
+        if (p.splits > 1) {
+            float *w = p.ws + ((int64_t)split * p.M + grow) * p.N + gcol;
+            if (gcol + 4 <= p.N && (p.N & 3) == 0) {
+                *(f32x4 *)w = (f32x4){v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (gcol + e < p.N) w[e] = v[e];
+            }
+            continue;
+        }
+        float *c = (float *)p.C + (int64_t)grow * p.ldc + gcol;
+        if (p.c_vec && gcol + 4 <= p.N) {
+            float cin[4] = {0.f, 0.f, 0.f, 0.f};
+            if (p.beta != 0.f) {
+                const f32x4 ci = *(const f32x4 *)c;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cin[e] = ci[e];
+            }
+            epilogue_row<float, 4>(p, v, cin, gcol);
+            *(f32x4 *)c = (f32x4){v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (gcol + e < p.N) {
+                    const float cin = p.beta != 0.f ? c[e] : 0.f;
+                    c[e] = epilogue_value<float>(p, v[e], cin, gcol + e);
+                }
+            }
+        }
+    }
+}
+
 // Waves: (BM/WM) x (BN/WN) sub-tiles per K group, KSPLIT groups.  Group g
 // runs the 16-k steps [g*4/KSPLIT, (g+1)*4/KSPLIT) of every slab, so with a
 // 128 x 128 tile of 64 x 64 sub-tiles and KSPLIT = 2 each SIMD holds two
@@ -485,6 +570,11 @@ struct PipeOperandS {
 // wave keeps half of its blocks and hands the other half to its partner (the
 // same sub-tile in the other group).  A 256 x 128 tile gets its two waves per
 // SIMD from eight 64 x 64 sub-tiles instead (KSPLIT = 1).
+// fp32 K groups (one 32 x 32 block per wave, KSPLIT of 2 or 4): group g runs
+// the MFMA steps [g, g+1) * BK/(2*KSPLIT) of every slab, so a 32 x 32 tile
+// with four groups puts a wave on each SIMD of its CU; at the end every wave
+// stages its partial block in LDS and group g sums rows [g, g+1) * 32/KSPLIT
+// of its sub-tile over the groups, in increasing group order.
 // LB: bytes per lane of each direct load, 16, or 4 for rows that are not
 // 16-byte aligned.  TC: the element type of C and the bias (T, or fp32 for an
 // fp32 output of 16-bit operands).  FBK: the K slab of fp32 operands, 16 or
@@ -503,8 +593,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     constexpr int NB = TM * TN;                    // 32x32 blocks per wave
     constexpr int KPW = (PIPE_BK / 16) / KSPLIT;   // fp16: 16-k steps per wave per slab
     static_assert(KPW >= 1 && KPW * KSPLIT == PIPE_BK / 16, "K split");
-    static_assert(KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
-    static_assert(HALF || KSPLIT == 1, "fp32 runs without K groups");
+    static_assert(!HALF || KSPLIT == 1 || NB % 2 == 0, "blocks split between partners");
+    static_assert(HALF || KSPLIT == 1 || ((KSPLIT == 2 || KSPLIT == 4) && NB == 1 && (FBK / 8) % KSPLIT == 0),
+                  "fp32 K groups: one block per wave, whole 4-step fragment groups per group");
     static_assert(FBK == 16 || (!HALF && FBK == 32), "fp32 slabs of 16 or 32");
     typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW, LB>, PipeOperandS<BM, !TA, NW, LB, FBK>>::type OpA;
     typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW, LB>, PipeOperandS<BN, TB, NW, LB, FBK>>::type OpB;
@@ -514,7 +605,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     constexpr int XCHG_BYTES = NW * (NB / 2) * 4096;     // partner exchange
     constexpr int EPI_LD = 40;                           // floats per staged row (32 + 8)
     constexpr int EPI_BYTES = NW * 32 * EPI_LD * 4;      // epilogue staging, one block per wave
-    static_assert(KSPLIT == 1 || XCHG_BYTES <= SMEM, "exchange fits the ring");
+    static_assert(!HALF || KSPLIT == 1 || XCHG_BYTES <= SMEM, "exchange fits the ring");
     static_assert(EPI_BYTES <= SMEM, "epilogue staging fits the ring");
     __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     lds_char_t *smem = (lds_char_t *)smem_raw;
@@ -841,10 +932,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
             }
             const lds_char_t *sA = smem + stage * STAGE_BYTES;
             const lds_char_t *sB = sA + OpA::BYTES;
-            constexpr int NM = (BK / 2) * TM * TN;
-            // BK/2 MFMA steps of k = 2 per slab, fragments 4 steps at a time
+            constexpr int C2W = (BK / 8) / KSPLIT;   // fragment groups of this wave per slab
+            constexpr int NM = C2W * 4 * TM * TN;
+            // BK/2 MFMA steps of k = 2 per slab, fragments 4 steps at a time;
+            // K group g takes fragment groups [g, g+1) * C2W
 #pragma unroll
-            for (int c2 = 0; c2 < BK / 8; ++c2) {
+            for (int cc = 0; cc < C2W; ++cc) {
+                const int c2 = (KSPLIT == 1 ? 0 : kgroup * C2W) + cc;
                 f32x4 a[TM], b[TN];
 #pragma unroll
                 for (int i = 0; i < TM; ++i) a[i] = ga.frag4(sA, wm0 + 32 * i, c2, lane);
@@ -856,7 +950,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
                         for (int j = 0; j < TN; ++j) {
-                            const int m = ((c2 * 4 + e) * TM + i) * TN + j;
+                            const int m = ((cc * 4 + e) * TM + i) * TN + j;
 #pragma unroll
                             for (int l = 0; l < LOADS; ++l) {
                                 if (l * NM / LOADS == m && spread) {
@@ -898,6 +992,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     // Each wave writes the blocks it does not own to its exchange slot, in
     // increasing q, 16 bytes per lane per 4 registers.
     __syncthreads();  // every wave is done with the ring
+    if constexpr (!HALF && KSPLIT > 1) {
+        fp32_groups_epilogue<KSPLIT, NWG, WAVES_N, WM, WN, EPI_LD>(p, smem, acc[0][0], wave, lane, m0, n0, split);
+        return;
+    }
     if constexpr (KSPLIT == 2) {
         lds_char_t *mine = smem + wave * (NB / 2) * 4096;
         const lds_char_t *theirs = smem + ((wave + NWG) % NW) * (NB / 2) * 4096;

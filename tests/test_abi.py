@@ -224,18 +224,28 @@ def test_fp32_tile_by_rounds():
                           (4096, 4224, 4096, (64, 64)), (2560, 2560, 2560, (64, 64)),
                           (3584, 3584, 3584, (64, 64)), (2304, 2048, 2048, (64, 64))):
         assert tile_of(M, N, K, 0) == tile, (M, N, K)
-    # at most one 128x128 tile per CU: the 64x64 tile, every transpose pair
-    # (the tall-skinny 8192x256x8192 of the full-form workload, 512^3, 2048^3);
+    # at most one 128x128 tile per CU and at least one 64x64 tile per CU: the
+    # 64x64 tile, every transpose pair (the tall-skinny 8192x256x8192 of the
+    # full-form workload, 1024^3, 2048^3);
     # 32-deep slabs in three stages (three workgroups per CU) unless the grid
     # has 769 to 1024 tiles, which four 16-deep workgroups per CU hold in one
     # round
     for M, N, K, name in ((8192, 256, 8192, "f32_64x64_pipe3_k32_mfma32x32x2"),
-                          (512, 512, 512, "f32_64x64_pipe3_k32_mfma32x32x2"),
+                          (1024, 1024, 1024, "f32_64x64_pipe3_k32_mfma32x32x2"),
                           (2048, 2048, 2048, "f32_64x64_pipe4_mfma32x32x2"),
                           (1792, 1792, 2048, "f32_64x64_pipe4_mfma32x32x2"),
                           (256, 8192, 8192, "f32_64x64_pipe3_k32_mfma32x32x2"),
                           (3072, 1024, 2048, "f32_64x64_pipe3_k32_mfma32x32x2"),
                           (2304, 2048, 2048, "f32_64x64_pipe3_k32_mfma32x32x2")):
+        for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            lda, ldb = (M if ta else K) + 8, (K if tb else N) + 8
+            k = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 8, 0)
+            assert dg.dg_kernel_name(k) == name, (M, N, K, ta, tb)
+    # fewer 64x64 tiles than CUs: the 32x32 tile with four K groups, four
+    # stages from K = 4096
+    for M, N, K in ((512, 512, 512), (256, 256, 256), (768, 768, 768), (512, 512, 8192), (900, 900, 64),
+                    (64, 4096, 1024), (128, 128, 4092), (128, 128, 4096)):
+        name = f"f32_32x32_pipe{4 if K >= 4096 else 3}_k32_ksplit4_mfma32x32x2"
         for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
             lda, ldb = (M if ta else K) + 8, (K if tb else N) + 8
             k = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 8, 0)

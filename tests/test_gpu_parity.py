@@ -127,6 +127,25 @@ def test_f32_64x64_steady_state_gates(dg, ta, tb, tiles_mn):
         check_full(p, kernel=k)
 
 
+@pytest.mark.parametrize("ta,tb", TRANS)
+@pytest.mark.parametrize("shape", [(32, 32, 32), (4, 4, 5), (36, 92, 1), (100, 68, 31), (64, 64, 33),
+                                   (300, 260, 257), (512, 252, 4099)])
+def test_f32_32x32_k_groups(dg, ta, tb, shape):
+    """The fp32 32x32 tile whose four waves each run a quarter of every
+    32-deep slab (three and four stages): ragged M and N around the 32-wide
+    tile, K of one element, a partial last slab, many slabs; the four
+    partial blocks summed in LDS before alpha, beta and C."""
+    M, N, K = shape
+    a, b, c0 = synth.problem(M, N, K, "f32", "uniform", 200 + 2 * ta + tb, with_c0=True)
+    pad = tuple((-x) % 4 + 4 for x in ((M if ta else K), (K if tb else N), N))
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, "f32", pad)
+    for name in ("f32_32x32_pipe3_k32_ksplit4_mfma32x32x2", "f32_32x32_pipe4_k32_ksplit4_mfma32x32x2"):
+        k = dg.kernel_names().index(name)
+        print(f"kernel {name} {shape} ta={ta} tb={tb}", flush=True)
+        assert pipe_ok(p)
+        check_full(p, kernel=k)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_unaligned_pointers(dg, dtype):
     M, N, K = 129, 257, 77
