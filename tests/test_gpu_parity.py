@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import Problem, check_full
+from gpu_util import DTYPES, Problem, check_full
 
 pytestmark = pytest.mark.gpu
 TRANS = list(itertools.product([False, True], [False, True]))
@@ -144,6 +144,39 @@ def test_f32_32x32_k_groups(dg, ta, tb, shape):
         print(f"kernel {name} {shape} ta={ta} tb={tb}", flush=True)
         assert pipe_ok(p)
         check_full(p, kernel=k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f16o32"])
+def test_dispatch_random_shapes(dg, dtype):
+    """The library's own kernel choice (dg_gemm) on 14 seeded random problems
+    per dtype: M, N, K drawn in 1..320 (a third of them multiples of 32, the
+    tile edges), a random transpose pair, row strides padded by 0, 8 or 16
+    elements in half the cases (16-byte rows when the extents allow: the
+    pipelined kernels) and by 0 to 9 in the others (mostly unaligned rows),
+    alpha in [-2, 2) and beta 0 or in [-1, 1).  Every output against the
+    oracle; the kernel chosen is printed with each case."""
+    rng = np.random.default_rng(2024 + ["f32", "f16", "bf16", "f16o32"].index(dtype))
+    dist = "uniform" if dtype == "f32" else "normal_sqrtk"
+    for case in range(14):
+        dims = [int(x) for x in rng.integers(1, 321, 3)]
+        if case % 3 == 0:
+            dims = [32 * max(1, d // 32) for d in dims]
+        ta, tb = bool(rng.integers(2)), bool(rng.integers(2))
+        if case % 4 < 2:
+            dims = [8 * max(1, d // 8) for d in dims]
+            pad = tuple(8 * int(x) for x in rng.integers(0, 3, 3))
+        else:
+            pad = tuple(int(x) for x in rng.integers(0, 10, 3))
+        M, N, K = dims
+        alpha = float(rng.uniform(-2, 2))
+        beta = 0.0 if case % 2 else float(rng.uniform(-1, 1))
+        a, b, c0 = synth.problem(M, N, K, dtype, dist, 300 + case, with_c0=True)
+        p = Problem(a, b, c0, ta, tb, alpha, beta, dtype, pad)
+        # device buffers start 256-byte aligned, as these stand-in addresses
+        name = dg.dg_kernel_name(dg.dg_select_kernel(ta, tb, M, N, K, 256, p.lda, 256, p.ldb, 256, p.ldc,
+                                                     DTYPES[dtype]))
+        print(f"case {case}: {dtype} {M}x{N}x{K} ta={ta} tb={tb} pad={pad} -> {name}", flush=True)
+        check_full(p, out=p.run_gpu())
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
