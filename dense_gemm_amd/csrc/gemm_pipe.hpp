@@ -663,7 +663,15 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     // bit-identical.
     constexpr bool FINE = HALF && BM == 256 && (BN == 256 || BN == 128);
     static_assert(!FINE || (STAGES == 2 && KSPLIT == 1), "the 256-row 16-bit loop uses two stages");
-    constexpr int PRO = FINE ? 1 : ((HALF && !LAG2) ? STAGES : STAGES - 1);
+    // The fp32 K-group loop below, which reads each slab's fragments one
+    // step ahead: for four stages (K >= 4096) and every transpose pair but
+    // tn.  Against the per-slab reads, one machine, bit-identical:
+    // 512^2x8192 nn/nt/tt 41.5/38.0/42.1 us against 54.1/41.9/53.0, 128^2x8192
+    // 41.1 against 53.4; tn 55.1 against 51.1 (both operands m/n-contiguous,
+    // eight 4-byte reads per fragment set); with three stages at K = 512
+    // (512^3, 256^3) 1-8% slower.
+    constexpr bool GROUPS32 = !HALF && KSPLIT > 1 && STAGES >= 4 && !(TA && !TB);
+    constexpr int PRO = FINE ? 1 : (((HALF && !LAG2) || GROUPS32) ? STAGES : STAGES - 1);
 #pragma unroll
     for (int s = 0; s < PRO; ++s) {
         if (s < nk) issue_slab(s, smem + s * STAGE_BYTES);
@@ -903,6 +911,91 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
         for (; kt < nk; kt += 2) {
             step(std::false_type(), kt, fa0, fb0, fa1, fb1);
             if (kt + 1 < nk) step(std::false_type(), kt + 1, fa1, fb1, fa0, fb0);
+        }
+    } else if constexpr (GROUPS32) {
+        // fp32 K groups: one wave per SIMD for each tile, so the fragment
+        // reads of a slab would sit between the barrier and the wave's first
+        // MFMA.  Instead step kt runs slab kt's MFMAs from registers and reads
+        // slab kt+1's fragments between them.  At its start the wave waits
+        // for slab kt+1 and meets the others at a barrier: slab kt+1 is then
+        // visible, and every wave holds slab kt's fragments, so slab kt's
+        // stage takes slab kt+STAGES (the prologue filled every stage).  The
+        // reads after the last slab fetch a stale stage that is never used.
+        constexpr int C2W = (BK / 8) / KSPLIT;    // fragment groups of this wave per slab
+        constexpr int NM = C2W * 4 * TM * TN;
+        f32x4 fa0[C2W][TM], fb0[C2W][TN], fa1[C2W][TM], fb1[C2W][TN];
+        auto readf = [&](int slab, f32x4(&fa)[C2W][TM], f32x4(&fb)[C2W][TN]) {
+            const lds_char_t *sA = smem + (slab % STAGES) * STAGE_BYTES;
+            const lds_char_t *sB = sA + OpA::BYTES;
+#pragma unroll
+            for (int cc = 0; cc < C2W; ++cc) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa[cc][i] = ga.frag4(sA, wm0 + 32 * i, kgroup * C2W + cc, lane);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fb[cc][j] = gb.frag4(sB, wn0 + 32 * j, kgroup * C2W + cc, lane);
+            }
+        };
+        auto gstep = [&](auto fast_tag, int kt, f32x4(&ca)[C2W][TM], f32x4(&cb)[C2W][TN], f32x4(&na)[C2W][TM],
+                         f32x4(&nb)[C2W][TN]) {
+            constexpr bool FAST = decltype(fast_tag)::value;
+            // slabs issued so far: [0, min(nk, kt + STAGES)); slab kt+1 must be complete
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (FAST) wait_vmcnt<(STAGES - 2) * LOADS>();
+            else if (kt + STAGES - 1 < nk) wait_vmcnt<(STAGES - 2) * LOADS>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            const int ns = kt + STAGES;
+            lds_char_t *dst = smem + (kt % STAGES) * STAGE_BYTES;      // slab kt's stage
+            const bool spread = FAST ? true : (ns < nk && !(ns == nk - 1 && krem < BK));
+            if constexpr (!FAST) {
+                if (ns < nk && !spread) issue_slab(ns, dst);
+            }
+            readf(kt + 1, na, nb);
+            // the reads go out before this slab's MFMAs (the compiler would
+            // otherwise sink them below the MFMAs and wait for them there)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cc = 0; cc < C2W; ++cc)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) {
+                            const int m = ((cc * 4 + e) * TM + i) * TN + j;
+#pragma unroll
+                            for (int l = 0; l < LOADS; ++l) {
+                                if (l * NM / LOADS == m && spread) {
+                                    if (l < OpA::LOADS) ga.issue_one(dst, wave, l);
+                                    else gb.issue_one(dst + OpA::BYTES, wave, l - OpA::LOADS);
+                                }
+                            }
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ca[cc][i][e], cb[cc][j][e], acc[i][j], 0, 0,
+                                                                             0);
+                        }
+            if (spread) {
+                ga.advance();
+                gb.advance();
+            }
+        };
+        if (nk > 0) {
+            // slab 0 complete; slabs 1 .. STAGES-1 may still be in flight
+            if (nk >= STAGES) wait_vmcnt<(STAGES - 1) * LOADS>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            readf(0, fa0, fb0);
+        }
+        // the steady state (the refilled slab a whole slab before the last)
+        // in a loop of its own, then the last steps
+        int kt = 0;
+        const int nfast = (krem == BK ? nk : nk - 1) - STAGES;
+        for (; kt + 1 < nfast; kt += 2) {
+            gstep(std::true_type(), kt, fa0, fb0, fa1, fb1);
+            gstep(std::true_type(), kt + 1, fa1, fb1, fa0, fb0);
+        }
+        for (; kt < nk; kt += 2) {
+            gstep(std::false_type(), kt, fa0, fb0, fa1, fb1);
+            if (kt + 1 < nk) gstep(std::false_type(), kt + 1, fa1, fb1, fa0, fb0);
         }
     } else {
         // One barrier per slab, at its start: slab kt is then in LDS for
