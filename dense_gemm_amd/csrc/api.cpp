@@ -327,14 +327,14 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
             // against 17.2, 512^2x2048 15.7 against 37.6, 512^2x8192 60
             // against 138; even at 256 tiles (1024^3 21.7 against 21.8,
             // 2048x512x512 13.1 against 13.3), 6% slower at 1024^2x4096.
-            // From K = 1024 the four-stage kernel, whose loop reads each
-            // slab's fragments one step ahead (nn, nt, tt): 512^2x1024
-            // nn/nt/tn/tt 8.1/7.5/8.9/8.2 us against 9.2/7.7/8.9/9.1 with
-            // three stages, 512^2x2048 12.8/11.7/15.0/13.0 against
-            // 15.7/12.6/15.0/15.5, 512^2x8192 41.3/37.8/50.8/41.9 against
-            // 59.8/48.9/62.7/59.8; at K = 512 three stages (512^3 1-4%
-            // faster).
-            if (pk == 3 && t64 < 256) return K >= 1024 ? K_F32_PIPE_32_KG4_S4 : K_F32_PIPE_32_KG4;
+            // From K = 512 the four-stage kernel, whose loop reads each
+            // slab's fragments one step ahead (nn, nt, tt): 512^3 nn/nt/tn/tt
+            // 5.93/5.58/6.13/6.02 us against 6.23/5.52/6.02/6.20 with three
+            // stages, 768^3 nn 13.4 against 14.2, 512^2x1024 8.1/7.5/8.9/8.2
+            // against 9.2/7.7/8.9/9.1, 512^2x8192 41.3/37.8/50.8/41.9 against
+            // 59.8/48.9/62.7/59.8; below K = 512 three stages (1-5% faster at
+            // K = 128 and 256).
+            if (pk == 3 && t64 < 256) return K >= 512 ? K_F32_PIPE_32_KG4_S4 : K_F32_PIPE_32_KG4;
             if (pk == 3 && (t64 <= 768 || t64 > 1024)) return K_F32_PIPE_64_K32;
             return pipe16[pk];
         }

@@ -242,10 +242,10 @@ def test_fp32_tile_by_rounds():
             k = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 8, 0)
             assert dg.dg_kernel_name(k) == name, (M, N, K, ta, tb)
     # fewer 64x64 tiles than CUs: the 32x32 tile with four K groups, four
-    # stages from K = 1024
+    # stages from K = 512
     for M, N, K in ((512, 512, 512), (256, 256, 256), (768, 768, 768), (512, 512, 8192), (900, 900, 64),
-                    (64, 4096, 1024), (128, 128, 1020), (128, 128, 4096)):
-        name = f"f32_32x32_pipe{4 if K >= 1024 else 3}_k32_ksplit4_mfma32x32x2"
+                    (64, 4096, 1024), (128, 128, 508), (128, 128, 4096)):
+        name = f"f32_32x32_pipe{4 if K >= 512 else 3}_k32_ksplit4_mfma32x32x2"
         for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
             lda, ldb = (M if ta else K) + 8, (K if tb else N) + 8
             k = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 8, 0)
