@@ -43,7 +43,8 @@ thread_local int g_last_hip_error = 0;
 //   PIPE:   direct-to-LDS pipelined kernels; 4 variants (transA x transB);
 //           need 16-byte aligned rows of A and B, and the m/n-contiguous
 //           operand's extent a multiple of 16 bytes.
-//   PIPE_DW: fp32 pipelined kernels with 4-byte direct loads; any fp32
+//   PIPE_DW: pipelined kernels with 4-byte direct loads (fp32: 16-byte
+//           ones for a k-contiguous operand in the _kw kernels); any fp32
 //           layout (4-byte aligned A and B).
 //   Both pipelined kinds address a tile's operands with 32-bit byte offsets.
 // `dtype` is the operand type (DG_F32, DG_F16_F32ACC or DG_BF16_F32ACC); a
@@ -101,6 +102,8 @@ const Family kFamilies[] = {
     {"f32_64x64_pipe3_k32_mfma32x32x2", DG_F32, 64, 64, 8, PIPE, dg::f32_pipe_launchers, 9},
     {"f32_32x32_pipe3_k32_ksplit4_mfma32x32x2", DG_F32, 32, 32, 8, PIPE, dg::f32_pipe_launchers, 10},
     {"f32_32x32_pipe4_k32_ksplit4_mfma32x32x2", DG_F32, 32, 32, 8, PIPE, dg::f32_pipe_launchers, 11},
+    {"f32_64x64_pipe4_kw_mfma32x32x2", DG_F32, 64, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 12},
+    {"f32_64x64_pipe3_k32_kw_mfma32x32x2", DG_F32, 64, 64, 8, PIPE_DW, dg::f32_pipe_launchers, 13},
 };
 constexpr int kNumKernels = sizeof(kFamilies) / sizeof(kFamilies[0]);
 enum {
@@ -113,7 +116,7 @@ enum {
     K_F32_PIPE_128_DW = 25, K_F16_PIPE_128_DW = 26, K_F16_PIPE_64_DW = 27, K_BF16_PIPE_128_DW = 28,
     K_BF16_PIPE_64_DW = 29, K_BF16_128 = 30, K_BF16_256 = 31, K_F32_PIPE_128x64 = 32,
     K_F32_PIPE_64 = 33, K_F32_PIPE_128x64_DW = 34, K_F32_PIPE_64_DW = 35, K_F32_PIPE_64_K32 = 36,
-    K_F32_PIPE_32_KG4 = 37, K_F32_PIPE_32_KG4_S4 = 38
+    K_F32_PIPE_32_KG4 = 37, K_F32_PIPE_32_KG4_S4 = 38, K_F32_PIPE_64_KW = 39, K_F32_PIPE_64_K32_KW = 40
 };
 
 constexpr int64_t kMaxBatch = 65535;   // a grid dimension
@@ -339,8 +342,17 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
             return pipe16[pk];
         }
         // rows not 16-byte aligned: the same tiles with 4-byte direct loads
-        // (the 32-deep slab measured 38% slower with them: 4095x4097x1031)
-        if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) return pipe4[pk];
+        // (the 32-deep slab measured 38% slower with them: 4095x4097x1031).
+        // On the 64x64 tile a k-contiguous operand takes 16-byte loads all
+        // the same (its pieces never cross the end of a row), one machine,
+        // 4095x4097x1031 with ld + 8: nn and tt 320.5 / 320.7 us against
+        // 330.4 / 331.0 (16-deep), nt 307.4 against 345.9 (32-deep, both
+        // operands k-contiguous); 2047x2049x2051 3-14% faster.  tn has no
+        // k-contiguous operand and keeps the 4-byte kernel.
+        if (pipe_dw_ok(ta, tb, M, N, A, lda, B, ldb, dtype, x)) {
+            if (pk == 3 && !(ta && !tb)) return (!ta && tb) ? K_F32_PIPE_64_K32_KW : K_F32_PIPE_64_KW;
+            return pipe4[pk];
+        }
         return big >= 384 ? K_F32_256 : K_F32_128;
     }
     // 16-bit operands: the tile is picked by how many CUs its tiles fill

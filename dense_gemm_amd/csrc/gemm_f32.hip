@@ -40,6 +40,9 @@ const launch_fn *f32_launchers(int config)
 //   10: 32x32 tile, 3 stages of 32-deep slabs, four K groups of one 32x32
 //      wave (one wave per SIMD for each workgroup)
 //   11: config 10 with 4 stages
+//   12, 13: configs 6 and 9 for rows that are 4-byte aligned only: 16-byte
+//      direct loads for a k-contiguous operand, 4-byte ones for an
+//      m/n-contiguous one
 #define DG_PIPE4(BM, BN, WM, WN, ST)                                                                \
     {launch_pipe<float, BM, BN, WM, WN, false, false, ST, 1>, launch_pipe<float, BM, BN, WM, WN, false, true, ST, 1>, \
      launch_pipe<float, BM, BN, WM, WN, true, false, ST, 1>, launch_pipe<float, BM, BN, WM, WN, true, true, ST, 1>}
@@ -48,7 +51,7 @@ const launch_fn *f32_launchers(int config)
      launch_pipe<float, BM, BN, WM, WN, true, false, ST, 1, 4>, launch_pipe<float, BM, BN, WM, WN, true, true, ST, 1, 4>}
 const launch_fn *f32_pipe_launchers(int config)
 {
-    static const launch_fn table[12][4] = {
+    static const launch_fn table[14][4] = {
         {launch_pipe<float, 256, 128, 128, 64, false, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, false, true, 3, 1>,
          launch_pipe<float, 256, 128, 128, 64, true, false, 3, 1>, launch_pipe<float, 256, 128, 128, 64, true, true, 3, 1>},
         {launch_pipe<float, 256, 256, 128, 64, false, false, 4, 1>, launch_pipe<float, 256, 256, 128, 64, false, true, 4, 1>,
@@ -73,6 +76,14 @@ const launch_fn *f32_pipe_launchers(int config)
          launch_pipe<float, 32, 32, 32, 32, false, true, 4, 4, 16, float, 32>,
          launch_pipe<float, 32, 32, 32, 32, true, false, 4, 4, 16, float, 32>,
          launch_pipe<float, 32, 32, 32, 32, true, true, 4, 4, 16, float, 32>},
+        {launch_pipe<float, 64, 64, 32, 32, false, false, 4, 1, 16, float, 16, 4>,
+         launch_pipe<float, 64, 64, 32, 32, false, true, 4, 1, 16, float, 16, 4>,
+         launch_pipe<float, 64, 64, 32, 32, true, false, 4, 1, 16, float, 16, 4>,
+         launch_pipe<float, 64, 64, 32, 32, true, true, 4, 1, 16, float, 16, 4>},
+        {launch_pipe<float, 64, 64, 32, 32, false, false, 3, 1, 16, float, 32, 4>,
+         launch_pipe<float, 64, 64, 32, 32, false, true, 3, 1, 16, float, 32, 4>,
+         launch_pipe<float, 64, 64, 32, 32, true, false, 3, 1, 16, float, 32, 4>,
+         launch_pipe<float, 64, 64, 32, 32, true, true, 3, 1, 16, float, 32, 4>},
     };
     return table[config];
 }

@@ -576,11 +576,15 @@ __device__ __forceinline__ void fp32_groups_epilogue(const GemmParams &p, lds_ch
 // stages its partial block in LDS and group g sums rows [g, g+1) * 32/KSPLIT
 // of its sub-tile over the groups, in increasing group order.
 // LB: bytes per lane of each direct load, 16, or 4 for rows that are not
-// 16-byte aligned.  TC: the element type of C and the bias (T, or fp32 for an
+// 16-byte aligned.  LBMN (default LB): the same for an m/n-contiguous
+// operand alone; LB = 16 with LBMN = 4 serves rows that are 4-byte aligned
+// only: the k-contiguous operand's 16-byte pieces lie inside its rows (its
+// K tail goes through registers) and need no 16-byte alignment, while an
+// m/n-contiguous extent that is not a multiple of 4 needs element loads.  TC: the element type of C and the bias (T, or fp32 for an
 // fp32 output of 16-bit operands).  FBK: the K slab of fp32 operands, 16 or
 // 32 (16-bit operands always take 64).
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
-          int LB = 16, typename TC = T, int FBK = 16>
+          int LB = 16, typename TC = T, int FBK = 16, int LBMN = LB>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_pipe_kernel(GemmParams p)
 {
     constexpr bool HALF = sizeof(T) == 2;          // fp16 or bf16 operands
@@ -597,8 +601,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
     static_assert(HALF || KSPLIT == 1 || ((KSPLIT == 2 || KSPLIT == 4) && NB == 1 && (FBK / 8) % KSPLIT == 0),
                   "fp32 K groups: one block per wave, whole 4-step fragment groups per group");
     static_assert(FBK == 16 || (!HALF && FBK == 32), "fp32 slabs of 16 or 32");
-    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW, LB>, PipeOperandS<BM, !TA, NW, LB, FBK>>::type OpA;
-    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW, LB>, PipeOperandS<BN, TB, NW, LB, FBK>>::type OpB;
+    // LB: bytes per direct load of a k-contiguous operand; LBMN: of an
+    // m/n-contiguous one
+    constexpr int LBA = TA ? LBMN : LB, LBB = TB ? LB : LBMN;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BM, !TA, NW, LBA>, PipeOperandS<BM, !TA, NW, LBA, FBK>>::type OpA;
+    typedef typename std::conditional<HALF, PipeOperandH<T, BN, TB, NW, LBB>, PipeOperandS<BN, TB, NW, LBB, FBK>>::type OpB;
     constexpr int BK = OpA::BK;
     constexpr int STAGE_BYTES = OpA::BYTES + OpB::BYTES;
     constexpr int SMEM = STAGES * STAGE_BYTES;
@@ -1292,13 +1299,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN) * KSPLIT, 2) void gemm_p
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool TA, bool TB, int STAGES, int KSPLIT,
-          int LB = 16, typename TC = T, int FBK = 16>
+          int LB = 16, typename TC = T, int FBK = 16, int LBMN = LB>
 hipError_t launch_pipe(const GemmParams &p, hipStream_t s)
 {
     const unsigned nwg = (unsigned)p.tiles_m * (unsigned)p.tiles_n * (unsigned)(p.splits > 1 ? p.splits : 1);
     GemmParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT, LB, TC, FBK>,
+    return hipLaunchKernel((const void *)&gemm_pipe_kernel<T, BM, BN, WM, WN, TA, TB, STAGES, KSPLIT, LB, TC, FBK, LBMN>,
                            dim3(nwg, p.batch), dim3(64 * (BM / WM) * (BN / WN) * KSPLIT), args, 0, s);
 }
 

@@ -100,9 +100,9 @@ def test_pipelined_kernels(dg, dtype, ta, tb, shape):
         print(f"kernel {name} {shape} ta={ta} tb={tb}", flush=True)
         out = run_or_unsupported(dg, p, k)
         if out is None:
-            assert not whole and "_dw_" not in name, name
+            assert not whole and "_dw_" not in name and "_kw_" not in name, name
             continue
-        assert whole or "_dw_" in name, name
+        assert whole or "_dw_" in name or "_kw_" in name, name
         check_full(p, kernel=k, out=out)
 
 
@@ -477,10 +477,12 @@ def _pad_4byte_rows(base, dtype):
 @pytest.mark.parametrize("ta,tb", TRANS)
 @pytest.mark.parametrize("shape", [(300, 258, 131), (130, 66, 70), (520, 514, 1030)])
 def test_four_byte_direct_loads(dg, dtype, ta, tb, shape):
-    """The library's own choice on row strides that rule out 16-byte loads:
-    a pipelined kernel with 4-byte loads (`_dw`), every output against the
-    oracle, alpha/beta applied, C's padding untouched.  Odd K puts a pair of
-    16-bit elements across the end of K in the last slab."""
+    """The library's own choice on row strides that rule out 16-byte
+    alignment: a pipelined kernel with 4-byte loads (`_dw`), or for fp32 on
+    the 64x64 tile 16-byte loads of a k-contiguous operand at 4-byte aligned
+    rows (`_kw`), every output against the oracle, alpha/beta applied, C's
+    padding untouched.  Odd K puts a pair of 16-bit elements across the end
+    of K in the last slab."""
     M, N, K = shape
     dist = "uniform" if dtype == "f32" else "normal_sqrtk"
     a, b, c0 = synth.problem(M, N, K, dtype, dist, 540 + M + K, with_c0=True)
@@ -489,7 +491,8 @@ def test_four_byte_direct_loads(dg, dtype, ta, tb, shape):
     p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype, pad=(pa, pb, 3))
     k = dg.dg_select_kernel(int(ta), int(tb), M, N, K, 256, p.lda, 256, p.ldb, 256, p.ldc,
                             {"f32": 0, "f16": 1, "bf16": 2}[dtype])
-    assert "_dw_" in dg.dg_kernel_name(k), dg.dg_kernel_name(k)
+    name = dg.dg_kernel_name(k)
+    assert "_dw_" in name or (dtype == "f32" and "_kw_" in name), name
     print(f"4-byte loads {dtype} {shape} ta={ta} tb={tb} lda={p.lda} ldb={p.ldb} "
           f"kernel={dg.dg_kernel_name(k)}", flush=True)
     check_full(p, out=p.run_gpu())
