@@ -25,7 +25,9 @@ matrix-core rate the control probe measures on the same box.  `control` holds
 the control benchmarks (matrix-core peak with the shader clock under load, and
 a plain copy) and whether they are within 10% of their references;
 `per_launch_us` and `cold_us` give per-launch medians, best and worst, and the
-median after a 512 MiB cache scrub.  `cpu_baseline` times the CPU oracle
+median after a 512 MiB cache scrub.  `power` holds the board's socket power
+and shader clock (from amd-smi) while fp32 4096^3, fp16 2048^3 nn and the
+fp16 matrix-core probe run back to back for 4 s each.  `cpu_baseline` times the CPU oracle
 (plain fp64 triple loop, the host cores this process may use) on a bounded
 sample of the same workload: whole rows of C.
 """
@@ -762,6 +764,66 @@ def smi_clocks(index=0):
         return None
 
 
+def power_under_load(fn, stream, seconds=4.0, skip=1.5, index=0):
+    """Board power and shader clock while `fn` (one launch) runs back to back
+    for `seconds`: `amd-smi metric --power --clock --json` in a child process,
+    called again and again from a host thread (about 10 samples a second).
+    The tool reports a window that lags the load by about a second, so
+    samples from the first `skip` seconds are dropped.  Returns the medians
+    of the socket power (W) and of the XCDs' current shader clocks (MHz), the
+    sample count and the mean time per launch over the window, or None when
+    the tool is missing or fails."""
+    import statistics
+    import subprocess
+    import threading
+
+    import torch
+    samples = []
+    stop = threading.Event()
+    t0 = time.perf_counter()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"],
+                                   capture_output=True, text=True, timeout=30)
+                data = json.loads(r.stdout)
+            except Exception:
+                return
+            if time.perf_counter() - t0 < skip:
+                continue
+            gpus = data["gpu_data"] if isinstance(data, dict) else data
+            g = next((x for x in gpus if x.get("gpu") == index), None)
+            if g is None:
+                return
+            pw = g.get("power", {}).get("socket_power", {})
+            clk = [v["clk"]["value"] for k, v in g.get("clock", {}).items()
+                   if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+            if isinstance(pw, dict) and isinstance(pw.get("value"), (int, float)) and clk:
+                samples.append((pw["value"], statistics.median(clk)))
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    n = 0
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            fn()
+        n += 50
+        torch.cuda.synchronize()
+    end.record(stream)
+    end.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"socket_power_w": statistics.median(p for p, _ in samples),
+            "gfx_mhz": statistics.median(c for _, c in samples), "samples": len(samples),
+            "us_per_launch": round(start.elapsed_time(end) * 1e3 / n, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -784,6 +846,8 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache launches (for hardware-counter passes, whose "
                          "per-kernel averages would otherwise mix cold and warm launches)")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the board power and clock samples under sustained load")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 256 MiB device-to-device copy (a kernel of known traffic, "
                          "to scale hardware byte counters)")
@@ -926,6 +990,40 @@ def main():
             del ref, ab
         out["fp16_2048"] = {"peak": PEAK_F16, "unit": "TFLOP/s", **res}
         del outs
+
+    # ---- board power and shader clock under sustained load ---------------------
+    # (the fp16 matrix rate on this workload's data is set by the power and
+    # clock the part holds, not by the specification's 2.4 GHz)
+    if not args.no_power:
+        pw = {"source": "amd-smi metric --power --clock: socket power and the median of the XCDs' "
+                        "shader clocks, medians over the samples of a 4 s window of back-to-back "
+                        "launches after its first 1.5 s"}
+        pw["fp32_4096_nn"] = power_under_load(step, stream)
+        if not args.no_f16:
+            An = torch.from_numpy(a16).to(dev)
+            Bn = torch.from_numpy(b16).to(dev)
+            Cn = torch.empty((S, S), dtype=torch.float16, device=dev)
+
+            def step16nn():
+                rc = dg.dg_gemm(0, 0, S, S, S, 1.0, An.data_ptr(), S, Bn.data_ptr(), S, 0.0,
+                                Cn.data_ptr(), S, dg.DG_F16_F32ACC, sptr)
+                if rc != 0:
+                    raise dg.GemmError(rc)
+            pw["fp16_2048_nn"] = power_under_load(step16nn, stream)
+            del An, Bn, Cn
+            import dense_gemm_amd.probe as pr
+            wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+            sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+            clk = torch.zeros(wgs * 2, dtype=torch.int64, device=dev)
+            for name, kind in (("mfma_f16_probe_random_operands", pr.DGP_MFMA_F16_RANDOM),
+                               ("mfma_f16_probe_constant_operands", pr.DGP_MFMA_F16)):
+                def pf(kind=kind):
+                    rc = pr.dgp_mfma_peak(kind, wgs, 2000, sink.data_ptr(), clk.data_ptr(), sptr)
+                    if rc != 0:
+                        raise RuntimeError(f"dgp_mfma_peak failed ({rc})")
+                pw[name] = power_under_load(pf, stream)
+            del sink, clk
+        out["power"] = pw
 
     # ---- bf16 2048^3 nn / tn / nt (same recipe as fp16) ------------------------
     if not args.no_f16:
