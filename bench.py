@@ -764,6 +764,28 @@ def smi_clocks(index=0):
         return None
 
 
+def parse_power_clock(text, index=0):
+    """(socket power in W, median of the XCDs' current shader clocks in MHz)
+    of GPU `index` from the JSON that `amd-smi metric --power --clock --json`
+    prints, or None when either is missing."""
+    import statistics
+    try:
+        data = json.loads(text)
+    except ValueError:
+        return None
+    gpus = data["gpu_data"] if isinstance(data, dict) else data
+    g = next((x for x in gpus if isinstance(x, dict) and x.get("gpu") == index), None)
+    if g is None:
+        return None
+    pw = g.get("power", {}).get("socket_power", {})
+    clk = [v["clk"]["value"] for k, v in g.get("clock", {}).items()
+           if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+           and isinstance(v["clk"].get("value"), (int, float))]
+    if not isinstance(pw, dict) or not isinstance(pw.get("value"), (int, float)) or not clk:
+        return None
+    return pw["value"], statistics.median(clk)
+
+
 def power_under_load(fn, stream, seconds=4.0, skip=1.5, index=0):
     """Board power and shader clock while `fn` (one launch) runs back to back
     for `seconds`: `amd-smi metric --power --clock --json` in a child process,
@@ -787,20 +809,14 @@ def power_under_load(fn, stream, seconds=4.0, skip=1.5, index=0):
             try:
                 r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"],
                                    capture_output=True, text=True, timeout=30)
-                data = json.loads(r.stdout)
             except Exception:
                 return
             if time.perf_counter() - t0 < skip:
                 continue
-            gpus = data["gpu_data"] if isinstance(data, dict) else data
-            g = next((x for x in gpus if x.get("gpu") == index), None)
-            if g is None:
+            pc = parse_power_clock(r.stdout, index)
+            if pc is None:
                 return
-            pw = g.get("power", {}).get("socket_power", {})
-            clk = [v["clk"]["value"] for k, v in g.get("clock", {}).items()
-                   if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
-            if isinstance(pw, dict) and isinstance(pw.get("value"), (int, float)) and clk:
-                samples.append((pw["value"], statistics.median(clk)))
+            samples.append(pc)
 
     th = threading.Thread(target=sampler)
     th.start()

@@ -46,6 +46,29 @@ def test_smi_clock_parser_failures(monkeypatch):
     assert bench.smi_clocks() is None
 
 
+def test_power_clock_parser():
+    """The socket power and the median of the XCDs' shader clocks, from the
+    layout `amd-smi metric --power --clock --json` prints (voltages and
+    throttle status reported as N/A; non-gfx clocks ignored)."""
+    clk = lambda v: {"value": v, "unit": "MHz"}
+    clock = {f"gfx_{i}": {"clk": clk(1880 + i), "min_clk": clk(500), "max_clk": clk(2400)} for i in range(8)}
+    clock["mem_0"] = {"clk": clk(2000)}
+    clock["fclk_0"] = {"clk": "N/A"}
+    power = {"socket_power": {"value": 1244, "unit": "W"}, "gfx_voltage": "N/A", "throttle_status": "N/A"}
+    text = json.dumps({"gpu_data": [{"gpu": 1, "power": {"socket_power": {"value": 99, "unit": "W"}}, "clock": clock},
+                                     {"gpu": 0, "power": power, "clock": clock}]})
+    assert bench.parse_power_clock(text) == (1244, 1883.5)
+    assert bench.parse_power_clock(text, index=1) == (99, 1883.5)
+    # a list at the top level, as older versions of the tool print
+    assert bench.parse_power_clock(json.dumps([{"gpu": 0, "power": power, "clock": clock}])) == (1244, 1883.5)
+    # missing readings and unparsable output
+    assert bench.parse_power_clock(json.dumps({"gpu_data": [{"gpu": 0, "power": {"socket_power": "N/A"},
+                                                             "clock": clock}]})) is None
+    assert bench.parse_power_clock(json.dumps({"gpu_data": [{"gpu": 0, "power": power, "clock": {}}]})) is None
+    assert bench.parse_power_clock(json.dumps({"gpu_data": [{"gpu": 3, "power": power, "clock": clock}]})) is None
+    assert bench.parse_power_clock("not json") is None
+
+
 def test_committed_counters_cover_the_bench_kernel():
     """The committed counter summary has the bench kernel's entry, at least
     its algorithmic bytes.  When it was taken from other kernel sources than
