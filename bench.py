@@ -27,7 +27,8 @@ a plain copy) and whether they are within 10% of their references;
 `per_launch_us` and `cold_us` give per-launch medians, best and worst, and the
 median after a 512 MiB cache scrub.  `power` holds the board's socket power
 and shader clock (from amd-smi) while fp32 4096^3, fp16 2048^3 nn and the
-fp16 matrix-core probe run back to back for 4 s each.  `cpu_baseline` times the CPU oracle
+fp16 matrix-core probe run back to back for 4 s each (skipped under a
+profiler, like the other amd-smi readings).  `cpu_baseline` times the CPU oracle
 (plain fp64 triple loop, the host cores this process may use) on a bounded
 sample of the same workload: whole rows of C.
 """
@@ -736,13 +737,23 @@ def slab_probe(dev, stream, slabs=2000):
             "gemm_tile_panels": gemm}
 
 
+def under_profiler():
+    """True when rocprofv3 runs this process (it exports ROCPROF_* variables).
+    Its library is preloaded into every child process too, where it can set
+    up the GPU before the child's own program starts; the amd-smi children
+    are skipped then."""
+    return any(k.startswith("ROCPROF_") for k in os.environ)
+
+
 def smi_clocks(index=0):
     """Clock state from `amd-smi metric --clock --json` (a child process): the
     median current shader clock over the XCDs, its range, whether it is
-    locked, and the memory clock.  None when the tool is missing or fails.
-    The tool starts in about a second, so it sees the GPU idle between
-    launches; the clock under load is the control probe's."""
+    locked, and the memory clock.  None when the tool is missing or fails,
+    or under a profiler.  The tool starts in about a second, so it sees the
+    GPU idle between launches; the clock under load is the control probe's."""
     import subprocess
+    if under_profiler():
+        return None
     try:
         r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
                            text=True, timeout=30)
@@ -1010,7 +1021,10 @@ def main():
     # ---- board power and shader clock under sustained load ---------------------
     # (the fp16 matrix rate on this workload's data is set by the power and
     # clock the part holds, not by the specification's 2.4 GHz)
-    if not args.no_power:
+    if not args.no_power and under_profiler():
+        out["power"] = {"skipped": "under a profiler (its library is preloaded into the amd-smi "
+                                   "child processes)"}
+    elif not args.no_power:
         pw = {"source": "amd-smi metric --power --clock: socket power and the median of the XCDs' "
                         "shader clocks, medians over the samples of a 4 s window of back-to-back "
                         "launches after its first 1.5 s"}

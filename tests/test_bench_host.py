@@ -83,3 +83,18 @@ def test_committed_counters_cover_the_bench_kernel():
         pytest.skip("profiles/hbm_traffic.txt was taken from other kernel sources")
     # at least the algorithmic bytes (A and B read once, C written once)
     assert traffic >= 3 * 4096 * 4096 * 4
+
+
+def test_amd_smi_children_skipped_under_profiler(monkeypatch):
+    """rocprofv3 exports ROCPROF_* variables; with one set, the clock reading
+    starts no amd-smi child process and returns None."""
+    for k in [k for k in os.environ if k.startswith("ROCPROF_")]:
+        monkeypatch.delenv(k)
+    assert not bench.under_profiler()
+    monkeypatch.setenv("ROCPROF_OUTPUT_PATH", "/tmp/x")
+    assert bench.under_profiler()
+
+    def no_child(*a, **k):
+        raise AssertionError("amd-smi started under a profiler")
+    monkeypatch.setattr(subprocess, "run", no_child)
+    assert bench.smi_clocks() is None
