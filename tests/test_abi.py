@@ -277,6 +277,22 @@ def test_pipelined_kernels_need_32bit_panel_offsets():
             assert ("pipe" in dg.dg_kernel_name(k)) == pipe, (dtype, ld, dg.dg_kernel_name(k))
 
 
+def test_forced_pipelined_kernel_refused_past_the_panel_limit():
+    # forcing a pipelined kernel on such a stride is refused before anything
+    # is enqueued (no device is touched, so this runs without a GPU)
+    names = dg.kernel_names()
+    for dtype, esize in ((dg.DG_F32, 4), (dg.DG_F16_F32ACC, 2), (dg.DG_BF16_F32ACC, 2)):
+        big = (1 << 31) // (256 * esize)
+        prefix = ("f32", "f16", "bf16")[dtype] + "_"
+        pipes = [i for i, n in enumerate(names) if n.startswith(prefix) and "pipe" in n]
+        assert pipes
+        for k in pipes:
+            for lda, ldb in ((big, 600), (600, big)):
+                rc = dg.dg_gemm_with_kernel(0, 0, 600, 600, 600, 1.0, 0x1000, lda, 0x2000, ldb,
+                                            0.0, 0x3000, 600, dtype, NULL, k)
+                assert rc == dg.DG_ERR_UNSUPPORTED, (names[k], lda, ldb, rc)
+
+
 def test_tile_grid_matches_the_pages_decompositions():
     """Output tiles of side T cover C[35,93] at ((35//T)*T, (93//T)*T): the
     8x8 tile at (32,88) entry (3,5) and the 64x64 tile at (0,64) of the pages

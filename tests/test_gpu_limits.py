@@ -1,7 +1,8 @@
 """Parity at the limits, on an MI355X through the C ABI: an output of more
 than 2^31 elements (64-bit offsets in every store path), thousands of
-batches in one call (the batch grid dimension), and a split-K over a very
-long K."""
+batches in one call (the batch grid dimension), a split-K over a very
+long K, and row strides at the pipelined kernels' 32-bit panel-offset limit
+(operands of more than 4 GiB on either side of it)."""
 import numpy as np
 import pytest
 
@@ -124,3 +125,55 @@ def test_panel_offsets_near_2_pow_31(dg, dtype):
     ref, ab = oracle.gemm(False, False, M, N, K, 1.0, a, K, b, N, 0.0, None, N)
     worst, bad = oracle.compare(dtype, got, ref, ab, 1.0, 0.0)
     assert bad == 0, worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_row_strides_at_the_panel_offset_limit(dg, dtype, ta, tb):
+    """A, B and C have 600 rows of the same stride ld, so each spans more
+    than 4 GiB.  With 256 rows just under 2^31 bytes (ld = limit - 64) the
+    dispatcher's kernel and the 256-row pipelined kernel run, the latter
+    addressing a k-contiguous panel with offsets up to about 2^31 from its
+    per-panel base.  At the limit the dispatcher takes a register-staged
+    kernel (64-bit addressing) and the pipelined one is refused.  Every output
+    against the oracle; C's padding keeps its NaN canaries."""
+    import torch
+    from gpu_util import DTYPES, OPND, OUTT, Problem, check_full, to_device, to_host, torch_dtype
+    dev = torch.device("cuda:0")
+    s = torch.cuda.current_stream(dev)
+    M = N = K = 600
+    esize = 4 if dtype == "f32" else 2
+    limit = (1 << 31) // (256 * esize)      # first stride whose 256 rows reach 2^31 bytes
+    wide = {"f32": "f32_256x128_pipe3_mfma32x32x2", "f16": "f16_256x128_pipe2_w8_mfma32x32x16"}[dtype]
+    wide = dg.kernel_names().index(wide)
+    a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 131, with_c0=True)
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype)      # compact operands for the oracle
+
+    def wide_buffer(x, st, ld):
+        buf = torch.full((x.shape[0], ld), float("nan"), dtype=torch_dtype(st), device=dev)
+        buf[:, :x.shape[1]] = to_device(x, st, dev).view(x.shape)
+        return buf
+
+    for ld in (limit - 64, limit):
+        A = wide_buffer(p.A, OPND[dtype], ld)
+        B = wide_buffer(p.B, OPND[dtype], ld)
+        C = wide_buffer(p.C0, OUTT[dtype], ld)
+        assert A.numel() * A.element_size() > 1 << 32
+        auto = dg.dg_select_kernel(ta, tb, M, N, K, A.data_ptr(), ld, B.data_ptr(), ld,
+                                   C.data_ptr(), ld, DTYPES[dtype])
+        assert ("pipe" in dg.dg_kernel_name(auto)) == (ld < limit), dg.dg_kernel_name(auto)
+        for k in (-1, wide):
+            C[:, :N] = to_device(p.C0, OUTT[dtype], dev).view(M, N)
+            print(f"\n  {dtype} {'t' if ta else 'n'}{'t' if tb else 'n'} ld={ld} kernel="
+                  f"{dg.dg_kernel_name(auto if k < 0 else k)}", flush=True)
+            rc = dg.dg_gemm_with_kernel(ta, tb, M, N, K, 1.5, A.data_ptr(), ld, B.data_ptr(), ld,
+                                        -0.5, C.data_ptr(), ld, DTYPES[dtype], s.cuda_stream, k)
+            if k == wide and ld >= limit:
+                assert rc == dg.DG_ERR_UNSUPPORTED, rc
+                continue
+            assert rc == 0, rc
+            s.synchronize()
+            assert torch.isnan(C[:, N:N + 64]).all() and torch.isnan(C[:, -64:]).all()
+            check_full(p, out=to_host(C[:, :N]))
+        del A, B, C
+        torch.cuda.empty_cache()
