@@ -206,6 +206,14 @@ int ex_position(int rc)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
+// Every row start of C (in every batch) on a 16-byte boundary: the epilogue
+// then reads and writes C in 16-byte pieces, else element by element.
+bool c_rows_vec(const void *C, int64_t ldc, int dtype, const Ext &x)
+{
+    const int64_t v = 16 / c_bytes(dtype);
+    return aligned16(C) && ldc % v == 0 && (x.batch <= 1 || x.sC % v == 0);
+}
+
 // 16-byte vector loads need every row start of A and B on a 16-byte boundary
 // (in every batch: the batch strides are whole 16-byte pieces too).
 bool vec_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype, const Ext &x)
@@ -267,7 +275,7 @@ int dw_kernel(int k, bool bf)
 // Kernel choice by dtype, preconditions and output tile count.  Larger tiles
 // re-read less of A and B; smaller tiles fill more of the 256 compute units.
 int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-           const void *B, int64_t ldb, int dtype, const Ext &x = Ext())
+           const void *B, int64_t ldb, int dtype, const Ext &x = Ext(), bool c_vec = true)
 {
     // the output type does not change the choice: the kernels are the same
     dtype = op_dtype(dtype);
@@ -298,15 +306,37 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         const int64_t t12864 = ceil_div(M, 128) * ceil_div(N, 64) * nb;
         const int64_t t64 = ceil_div(M, 64) * ceil_div(N, 64) * nb;
         int pk;                                    // 0: 256x128, 1: 128x128, 2: 128x64, 3: 64x64
+        const double cost[4] = {(big % 512 == 0) ? ceil_div(big, 256) * 1.933 : 1e30,
+                                (double)ceil_div(small, 256),
+                                ceil_div(t12864, 256) * 0.51, ceil_div(t64, 256) * 0.2636};
         if (small <= 256) {
             pk = 3;
         } else {
-            const double cost[4] = {(big % 512 == 0) ? ceil_div(big, 256) * 1.933 : 1e30,
-                                    (double)ceil_div(small, 256),
-                                    ceil_div(t12864, 256) * 0.51, ceil_div(t64, 256) * 0.2636};
             pk = 0;
             for (int c = 1; c < 4; ++c)
                 if (cost[c] < cost[pk]) pk = c;
+        }
+        // C rows not 16-byte aligned: the epilogue reads and writes C element
+        // by element.  On one or two rounds of 256x128 or 128x128 tiles every
+        // CU runs it at the same moment, at the end; on 128x64 and 64x64
+        // tiles it overlaps other tiles' loops.  One machine, alpha 1, beta 0
+        // or -0.5, all four transpose pairs, the better small tile against
+        // the model's large one: with 16-byte rows of A and B (ldc odd)
+        // 4096^2x1032, 4096x8192x1032 and 6144x4096x1032 3-20% faster,
+        // 4096^2x2048 2-6%; with 4-byte rows (ld + 8 or + 9) 4095x4096x1031,
+        // 4096x4095x1031, 4096x8191x1031 and 6144x4095x1031 6-18% faster,
+        // while from K = 2051 the large tiles stay ahead or within 3%
+        // (4096x4095x4095, 8192x4095x2051).  Which small tile depends on the
+        // loads: with 16-byte rows 64x64 for nn and nt (the 128x64 kernel
+        // was slower than 256x128 there), 128x64 for tn and tt; with 4-byte
+        // rows 128x64 for nn and tt, 64x64 for nt and tn.  Against the
+        // model's tile on grids of 2048x4096 to 6144^2 at K = 136 to 2048 the
+        // swap took 0.82-0.99 of the time in 51 of 56 cases, up to 1.06 in
+        // the others; below K = 512 only the 64x64 tile gains (0.83-0.98;
+        // 128x64 1.16-1.18 at K = 136), so 128x64 is taken from K = 512.
+        if (!c_vec && K <= 2048 && pk < 2) {
+            const int smaller = (pipe ? !ta : ta != tb) ? 3 : 2;
+            if (smaller == 3 || K >= 512) pk = smaller;
         }
         static const int pipe16[4] = {K_F32_PIPE_256x128, K_F32_PIPE_128, K_F32_PIPE_128x64, K_F32_PIPE_64};
         static const int pipe4[4] = {K_F32_PIPE_256x128_DW, K_F32_PIPE_128_DW, K_F32_PIPE_128x64_DW, K_F32_PIPE_64_DW};
@@ -485,8 +515,7 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     p.beta = beta;
     p.tiles_m = p.tiles_n = 0;
     p.group_m = 1;
-    const int64_t v = 16 / c_bytes(dtype);
-    p.c_vec = aligned16(C) && ldc % v == 0 && (x.batch <= 1 || x.sC % v == 0);
+    p.c_vec = c_rows_vec(C, ldc, dtype, x);
     p.splits = 1;
     p.k_chunk = 0;
     p.ws = nullptr;
@@ -504,7 +533,7 @@ int run(int ta, int tb, int64_t M, int64_t N, int64_t K, float alpha, const void
     if (K == 0 || alpha == 0.f) {
         err = dg::scale_launcher(di)(p, s);
     } else {
-        if (kernel == DG_KERNEL_AUTO) kernel = choose(ta, tb, M, N, K, A, lda, B, ldb, dtype, x);
+        if (kernel == DG_KERNEL_AUTO) kernel = choose(ta, tb, M, N, K, A, lda, B, ldb, dtype, x, p.c_vec);
         if (!supports(kernel, ta, tb, M, N, K, A, lda, B, ldb, dtype, x)) return DG_ERR_UNSUPPORTED;
         const Family &f = kFamilies[kernel];
         if (f.kind == SIMPLE) {
@@ -656,7 +685,8 @@ int dg_gemm_splitk_noalloc(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N,
     // holds are refused before anything is enqueued
     int used = 1;
     if (K > 0 && alpha != 0.f) {
-        const int k = choose(transA, transB, M, N, K, A, lda, B, ldb, dtype);
+        const int k = choose(transA, transB, M, N, K, A, lda, B, ldb, dtype, Ext(),
+                             c_rows_vec(C, ldc, dtype, Ext()));
         int32_t chunk;
         used = resolve_splits(kFamilies[k], M, N, K, splits, &chunk);
     }
@@ -698,7 +728,7 @@ int dg_select_kernel(dg_op_t transA, dg_op_t transB, int64_t M, int64_t N, int64
 {
     int rc = validate(transA, transB, M, N, K, 1.f, A, lda, B, ldb, C, ldc, dtype, false);
     if (rc) return rc;
-    return choose(transA, transB, M, N, K, A, lda, B, ldb, dtype, Ext());
+    return choose(transA, transB, M, N, K, A, lda, B, ldb, dtype, Ext(), c_rows_vec(C, ldc, dtype, Ext()));
 }
 
 int dg_kernel_count(void) { return kNumKernels; }

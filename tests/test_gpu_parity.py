@@ -179,6 +179,25 @@ def test_dispatch_random_shapes(dg, dtype):
         check_full(p, out=p.run_gpu())
 
 
+@pytest.mark.parametrize("ta,tb", TRANS)
+@pytest.mark.parametrize("aligned_ab", [True, False])
+def test_f32_unaligned_c_rows_route(dg, ta, tb, aligned_ab):
+    """The library's own choice for an fp32 C whose rows are not 16-byte
+    aligned (ldc = N + 1) at a short K, where the dispatcher takes a 128x64
+    or 64x64 tile instead of the tile model's 128x128: 2048x4096x520, alpha
+    1.5, beta -0.5, rows of A and B 16-byte aligned or not.  Every output
+    against the oracle, C's padding untouched."""
+    M, N, K = 2048, 4096, 520
+    a, b, c0 = synth.problem(M, N, K, "f32", "uniform", 140 + 2 * ta + tb, with_c0=True)
+    pad = (0, 0, 1) if aligned_ab else (9, 9, 1)
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, "f32", pad)
+    k = dg.dg_select_kernel(ta, tb, M, N, K, 256, p.lda, 256, p.ldb, 256, p.ldc, DTYPES["f32"])
+    name = dg.dg_kernel_name(k)
+    print(f"kernel {name} ta={ta} tb={tb} aligned A/B={aligned_ab}", flush=True)
+    assert "128x64" in name or "64x64" in name, name
+    check_full(p)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_unaligned_pointers(dg, dtype):
     M, N, K = 129, 257, 77
