@@ -413,6 +413,13 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // 5120x4096x2048 take 128x128 (a few 256x256 tiles past a round).
         // The two-workgroup 128x128 kernel measured slower than the
         // one-workgroup one at every such shape and is not chosen.
+        // C rows not 16-byte aligned: C goes through the epilogue element by
+        // element, 2-3x slower on every tile, and the one-round 256x256 and
+        // 256x128 grids run it on all CUs at once at the end.  fp16 C with
+        // ldc = N + 1, beta -0.5, nn/nt/tn, one machine: the 128x128 tile
+        // 3-43% faster than the model's tile (4096^2x1032, 4096x8192x1032,
+        // 2048x4096x520, 4096^3, 8192^2x1032; 256x256 2% ahead at 8192^2 nt).
+        if (big > 128 && !c_vec) return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;
         if (big > 128) {
             auto rounds = [](int64_t t) { return (double)(t / 256) + (t % 256 ? 0.82 : 0.0); };
             const double k = (double)K;

@@ -309,6 +309,21 @@ def test_fp32_unaligned_c_rows_take_the_smaller_tiles_at_short_k():
     assert name(0, 0, 4096, 4096, 4096, 256, 4096, 256, 4096, 256, 4097) == "f32_256x128_pipe3_mfma32x32x2"
 
 
+def test_16bit_unaligned_c_rows_take_the_128x128_tile():
+    # 16-bit C rows not 16-byte aligned: the 128x128 tile replaces the
+    # one-round 256x256 / 256x128 tiles of the model
+    for dtype, tile in ((dg.DG_F16_F32ACC, "f16_128x128_pipe4_ksplit2_mfma32x32x16"),
+                        (dg.DG_BF16_F32ACC, "bf16_128x128_pipe4_ksplit2_mfma32x32x16")):
+        for M, N, K in ((4096, 4096, 1032), (2048, 4096, 520), (4096, 4096, 4096), (8192, 8192, 1032)):
+            for ta, tb in ((0, 0), (0, 1), (1, 0), (1, 1)):
+                lda, ldb = (M if ta else K), (K if tb else N)
+                sel = lambda ldc: dg.dg_kernel_name(
+                    dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, ldc, dtype))
+                assert sel(N + 1) == tile, (dtype, M, N, K, ta, tb)
+                assert sel(N + 8) == sel(N)
+                assert "256x" in sel(N), sel(N)
+
+
 def test_forced_pipelined_kernel_refused_past_the_panel_limit():
     # forcing a pipelined kernel on such a stride is refused before anything
     # is enqueued (no device is touched, so this runs without a GPU)

@@ -198,6 +198,23 @@ def test_f32_unaligned_c_rows_route(dg, ta, tb, aligned_ab):
     check_full(p)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
+def test_16bit_unaligned_c_rows_route(dg, dtype, ta, tb):
+    """The library's own choice for a 16-bit C whose rows are not 16-byte
+    aligned (ldc = N + 1), where the dispatcher takes the 128x128 tile instead
+    of the model's 256x128: 2048x4096x520, alpha 1.5, beta -0.5.  Every
+    output against the oracle, C's padding untouched."""
+    M, N, K = 2048, 4096, 520
+    a, b, c0 = synth.problem(M, N, K, dtype, "normal_sqrtk", 150 + 2 * ta + tb, with_c0=True)
+    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype, (0, 0, 1))
+    k = dg.dg_select_kernel(ta, tb, M, N, K, 256, p.lda, 256, p.ldb, 256, p.ldc, DTYPES[dtype])
+    name = dg.dg_kernel_name(k)
+    print(f"kernel {name} {dtype} ta={ta} tb={tb}", flush=True)
+    assert "128x128" in name, name
+    check_full(p)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_unaligned_pointers(dg, dtype):
     M, N, K = 129, 257, 77
