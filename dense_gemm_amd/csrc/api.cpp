@@ -206,12 +206,15 @@ int ex_position(int rc)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-// Every row start of C (in every batch) on a 16-byte boundary: the epilogue
-// then reads and writes C in 16-byte pieces, else element by element.
+// Every row start of C (in every batch) on a 4-byte boundary: the epilogue
+// then reads and writes C in 16-byte pieces (whole multiples of 16 bytes from
+// a row start, so each access is at least 4-byte aligned: the same alignment
+// the k-contiguous operands' 16-byte direct loads run at), else element by
+// element.  Always so for an fp32 C; a 16-bit C needs an even ldc.
 bool c_rows_vec(const void *C, int64_t ldc, int dtype, const Ext &x)
 {
-    const int64_t v = 16 / c_bytes(dtype);
-    return aligned16(C) && ldc % v == 0 && (x.batch <= 1 || x.sC % v == 0);
+    const int64_t cb = c_bytes(dtype);
+    return ((uintptr_t)C & 3) == 0 && (ldc * cb) % 4 == 0 && (x.batch <= 1 || (x.sC * cb) % 4 == 0);
 }
 
 // 16-byte vector loads need every row start of A and B on a 16-byte boundary
@@ -316,28 +319,6 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
             for (int c = 1; c < 4; ++c)
                 if (cost[c] < cost[pk]) pk = c;
         }
-        // C rows not 16-byte aligned: the epilogue reads and writes C element
-        // by element.  On one or two rounds of 256x128 or 128x128 tiles every
-        // CU runs it at the same moment, at the end; on 128x64 and 64x64
-        // tiles it overlaps other tiles' loops.  One machine, alpha 1, beta 0
-        // or -0.5, all four transpose pairs, the better small tile against
-        // the model's large one: with 16-byte rows of A and B (ldc odd)
-        // 4096^2x1032, 4096x8192x1032 and 6144x4096x1032 3-20% faster,
-        // 4096^2x2048 2-6%; with 4-byte rows (ld + 8 or + 9) 4095x4096x1031,
-        // 4096x4095x1031, 4096x8191x1031 and 6144x4095x1031 6-18% faster,
-        // while from K = 2051 the large tiles stay ahead or within 3%
-        // (4096x4095x4095, 8192x4095x2051).  Which small tile depends on the
-        // loads: with 16-byte rows 64x64 for nn and nt (the 128x64 kernel
-        // was slower than 256x128 there), 128x64 for tn and tt; with 4-byte
-        // rows 128x64 for nn and tt, 64x64 for nt and tn.  Against the
-        // model's tile on grids of 2048x4096 to 6144^2 at K = 136 to 2048 the
-        // swap took 0.82-0.99 of the time in 51 of 56 cases, up to 1.06 in
-        // the others; below K = 512 only the 64x64 tile gains (0.83-0.98;
-        // 128x64 1.16-1.18 at K = 136), so 128x64 is taken from K = 512.
-        if (!c_vec && K <= 2048 && pk < 2) {
-            const int smaller = (pipe ? !ta : ta != tb) ? 3 : 2;
-            if (smaller == 3 || K >= 512) pk = smaller;
-        }
         static const int pipe16[4] = {K_F32_PIPE_256x128, K_F32_PIPE_128, K_F32_PIPE_128x64, K_F32_PIPE_64};
         static const int pipe4[4] = {K_F32_PIPE_256x128_DW, K_F32_PIPE_128_DW, K_F32_PIPE_128x64_DW, K_F32_PIPE_64_DW};
         if (pipe) {
@@ -413,10 +394,10 @@ int choose(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64
         // 5120x4096x2048 take 128x128 (a few 256x256 tiles past a round).
         // The two-workgroup 128x128 kernel measured slower than the
         // one-workgroup one at every such shape and is not chosen.
-        // C rows not 16-byte aligned: C goes through the epilogue element by
-        // element, 2-3x slower on every tile, and the one-round 256x256 and
-        // 256x128 grids run it on all CUs at once at the end.  fp16 C with
-        // ldc = N + 1, beta -0.5, nn/nt/tn, one machine: the 128x128 tile
+        // C rows not 4-byte aligned (odd ldc): C goes through the epilogue
+        // element by element, 2-3x slower on every tile, and the one-round
+        // 256x256 and 256x128 grids run it on all CUs at once at the end.
+        // fp16 C with ldc = N + 1, beta -0.5, nn/nt/tn, one machine: the 128x128 tile
         // 3-43% faster than the model's tile (4096^2x1032, 4096x8192x1032,
         // 2048x4096x520, 4096^3, 8192^2x1032; 256x256 2% ahead at 8192^2 nt).
         if (big > 128 && !c_vec) return bf ? K_BF16_PIPE_128 : K_F16_PIPE_128;

@@ -38,7 +38,7 @@ struct GemmParams {
     float alpha, beta;
     int32_t tiles_m, tiles_n;  // output tiles of the launch
     int32_t group_m;           // tile rows walked together (cache locality)
-    int32_t c_vec;             // C rows start on 16-byte boundaries (16-byte stores allowed)
+    int32_t c_vec;             // C rows start on 4-byte boundaries (16-byte accesses allowed)
     // split-K: with splits > 1 the grid is tiles x splits; workgroup (tile, s)
     // covers k in [s*k_chunk, min(K, (s+1)*k_chunk)) and writes its raw fp32
     // sums to ws[s][M][N] (row stride N) instead of C.

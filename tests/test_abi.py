@@ -277,41 +277,10 @@ def test_pipelined_kernels_need_32bit_panel_offsets():
             assert ("pipe" in dg.dg_kernel_name(k)) == pipe, (dtype, ld, dg.dg_kernel_name(k))
 
 
-def test_fp32_unaligned_c_rows_take_the_smaller_tiles_at_short_k():
-    # C rows not 16-byte aligned: element-wise epilogue, so up to K = 2048
-    # the 128x64 or 64x64 tile replaces the model's 256x128 / 128x128 one
-    name = lambda *a: dg.dg_kernel_name(dg.dg_select_kernel(*a, dg.DG_F32))
-    pairs = ((0, 0), (0, 1), (1, 0), (1, 1))
-    for M, N, K in ((4096, 4096, 1032), (6144, 4096, 1032), (4096, 4096, 2048)):
-        for ta, tb in pairs:
-            lda, ldb = (M if ta else K), (K if tb else N)
-            # 16-byte rows of A and B: 64x64 for nn and nt, 128x64 for tn and tt
-            want = "f32_128x64_pipe4_mfma32x32x2" if ta else "f32_64x64_pipe3_k32_mfma32x32x2"
-            assert name(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 1) == want, (M, N, K, ta, tb)
-            assert name(ta, tb, M, N, K, 256, lda, 256, ldb, 260, N) == want   # C itself unaligned
-            assert "pipe" in name(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N)
-            assert "128x64" not in name(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N)
-    for M, N, K in ((4095, 4096, 1031), (4096, 8191, 1031)):
-        for ta, tb in pairs:
-            lda, ldb = (M if ta else K) + 9, (K if tb else N) + 9
-            if lda % 4 == 0 and ldb % 4 == 0 and not (ta and M % 4):
-                continue                 # rows 16-byte aligned: the case above
-            want = ("f32_128x64_pipe4_dw_mfma32x32x2" if ta == tb else
-                    "f32_64x64_pipe3_k32_kw_mfma32x32x2" if tb else "f32_64x64_pipe4_dw_mfma32x32x2")
-            ldc = N + 8 if (N + 8) % 4 else N + 9
-            assert name(ta, tb, M, N, K, 256, lda, 256, ldb, 256, ldc) == want, (M, N, K, ta, tb)
-    # below K = 512 only a 64x64 swap is taken: 128x64 lost there
-    for ta, tb in pairs:
-        got = name(ta, tb, 4096, 2048, 136, 256, 4096 if ta else 136, 256, 136 if tb else 2048, 256, 2049)
-        assert got == ("f32_128x128_pipe4_mfma32x32x2" if ta else "f32_64x64_pipe3_k32_mfma32x32x2"), got
-    # longer K: the model's tile
-    assert name(0, 0, 4096, 4095, 4095, 256, 4103, 256, 4103, 256, 4103) == "f32_256x128_pipe3_dw_mfma32x32x2"
-    assert name(0, 0, 4096, 4096, 4096, 256, 4096, 256, 4096, 256, 4097) == "f32_256x128_pipe3_mfma32x32x2"
-
-
 def test_16bit_unaligned_c_rows_take_the_128x128_tile():
-    # 16-bit C rows not 16-byte aligned: the 128x128 tile replaces the
-    # one-round 256x256 / 256x128 tiles of the model
+    # 16-bit C rows not 4-byte aligned (odd ldc): the 128x128 tile replaces
+    # the one-round 256x256 / 256x128 tiles of the model; an even ldc keeps
+    # the 16-byte epilogue and the model's tile
     for dtype, tile in ((dg.DG_F16_F32ACC, "f16_128x128_pipe4_ksplit2_mfma32x32x16"),
                         (dg.DG_BF16_F32ACC, "bf16_128x128_pipe4_ksplit2_mfma32x32x16")):
         for M, N, K in ((4096, 4096, 1032), (2048, 4096, 520), (4096, 4096, 4096), (8192, 8192, 1032)):
@@ -320,7 +289,7 @@ def test_16bit_unaligned_c_rows_take_the_128x128_tile():
                 sel = lambda ldc: dg.dg_kernel_name(
                     dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, ldc, dtype))
                 assert sel(N + 1) == tile, (dtype, M, N, K, ta, tb)
-                assert sel(N + 8) == sel(N)
+                assert sel(N + 8) == sel(N + 2) == sel(N)
                 assert "256x" in sel(N), sel(N)
 
 

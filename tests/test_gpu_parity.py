@@ -179,32 +179,13 @@ def test_dispatch_random_shapes(dg, dtype):
         check_full(p, out=p.run_gpu())
 
 
-@pytest.mark.parametrize("ta,tb", TRANS)
-@pytest.mark.parametrize("aligned_ab", [True, False])
-def test_f32_unaligned_c_rows_route(dg, ta, tb, aligned_ab):
-    """The library's own choice for an fp32 C whose rows are not 16-byte
-    aligned (ldc = N + 1) at a short K, where the dispatcher takes a 128x64
-    or 64x64 tile instead of the tile model's 128x128: 2048x4096x520, alpha
-    1.5, beta -0.5, rows of A and B 16-byte aligned or not.  Every output
-    against the oracle, C's padding untouched."""
-    M, N, K = 2048, 4096, 520
-    a, b, c0 = synth.problem(M, N, K, "f32", "uniform", 140 + 2 * ta + tb, with_c0=True)
-    pad = (0, 0, 1) if aligned_ab else (9, 9, 1)
-    p = Problem(a, b, c0, ta, tb, 1.5, -0.5, "f32", pad)
-    k = dg.dg_select_kernel(ta, tb, M, N, K, 256, p.lda, 256, p.ldb, 256, p.ldc, DTYPES["f32"])
-    name = dg.dg_kernel_name(k)
-    print(f"kernel {name} ta={ta} tb={tb} aligned A/B={aligned_ab}", flush=True)
-    assert "128x64" in name or "64x64" in name, name
-    check_full(p)
-
-
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
 def test_16bit_unaligned_c_rows_route(dg, dtype, ta, tb):
-    """The library's own choice for a 16-bit C whose rows are not 16-byte
-    aligned (ldc = N + 1), where the dispatcher takes the 128x128 tile instead
-    of the model's 256x128: 2048x4096x520, alpha 1.5, beta -0.5.  Every
-    output against the oracle, C's padding untouched."""
+    """The library's own choice for a 16-bit C whose rows are not 4-byte
+    aligned (ldc = N + 1, element-wise epilogue), where the dispatcher takes
+    the 128x128 tile instead of the model's 256x128: 2048x4096x520, alpha
+    1.5, beta -0.5.  Every output against the oracle, C's padding untouched."""
     M, N, K = 2048, 4096, 520
     a, b, c0 = synth.problem(M, N, K, dtype, "normal_sqrtk", 150 + 2 * ta + tb, with_c0=True)
     p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype, (0, 0, 1))
@@ -213,6 +194,24 @@ def test_16bit_unaligned_c_rows_route(dg, dtype, ta, tb):
     print(f"kernel {name} {dtype} ta={ta} tb={tb}", flush=True)
     assert "128x128" in name, name
     check_full(p)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("extra", [1, 2, 6])
+def test_c_rows_4byte_aligned_take_16byte_accesses(dg, dtype, extra):
+    """C rows 4-byte but not 16-byte aligned (ldc = N + 2 or N + 6 for 16-bit
+    C; N + 1, 2, 6 for fp32) go through the epilogue's 16-byte loads and
+    stores; an odd 16-bit ldc (N + 1) through the element path.  Every kernel
+    of the type, beta != 0 (C read), ragged edges; every output against the
+    oracle, C's padding untouched."""
+    M, N, K = 300, 264, 200
+    a, b, c0 = synth.problem(M, N, K, dtype, "uniform", 160 + extra, with_c0=True)
+    for ta, tb in TRANS:
+        p = Problem(a, b, c0, ta, tb, 1.5, -0.5, dtype, (8, 8, extra))
+        for k in kernels_for(dg, dtype):
+            out = run_or_unsupported(dg, p, k)
+            if out is not None:
+                check_full(p, kernel=k, out=out)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
