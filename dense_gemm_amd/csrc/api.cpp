@@ -41,7 +41,7 @@ thread_local int g_last_hip_error = 0;
 //   MFMA:   register-staged matrix-core kernels, any shape; 8 variants:
 //           transA x transB x (16-byte vector loads or element loads).
 //   PIPE:   direct-to-LDS pipelined kernels; 4 variants (transA x transB);
-//           need 16-byte aligned rows of A and B, and the m/n-contiguous
+//           need 4-byte aligned rows of A and B, and the m/n-contiguous
 //           operand's extent a multiple of 16 bytes.
 //   PIPE_DW: pipelined kernels with 4-byte direct loads (fp32: 16-byte
 //           ones for a k-contiguous operand in the _kw kernels); any fp32
@@ -236,15 +236,25 @@ bool offsets_fit(int64_t lda, int64_t ldb, int dtype)
     return 256 * lda * elem_bytes(dtype) < lim && 256 * ldb * elem_bytes(dtype) < lim;
 }
 
-// Preconditions of the pipelined kernels (see Family): 16-byte aligned rows
+// Preconditions of the pipelined kernels (see Family): 4-byte aligned rows
 // of A and B, and the m/n-contiguous operand's extent a whole number of
 // 16-byte pieces.
+// The 16-byte direct loads of a tile sit at whole multiples of 16 bytes from
+// a row start, so they need every row start (in every batch) 4-byte aligned
+// only, as the k-contiguous operands' 16-byte loads at padded rows do.
+bool rows4_ok(const void *A, int64_t lda, const void *B, int64_t ldb, int dtype, const Ext &x)
+{
+    const int64_t eb = elem_bytes(dtype);
+    return ((uintptr_t)A & 3) == 0 && ((uintptr_t)B & 3) == 0 && (lda * eb) % 4 == 0 &&
+           (ldb * eb) % 4 == 0 && (x.batch <= 1 || ((x.sA * eb) % 4 == 0 && (x.sB * eb) % 4 == 0));
+}
+
 bool pipe_ok(int ta, int tb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
              const void *B, int64_t ldb, int dtype, const Ext &x)
 {
     const int64_t v = 16 / elem_bytes(dtype);
     (void)K;
-    return offsets_fit(lda, ldb, dtype) && vec_ok(A, lda, B, ldb, dtype, x) && (!ta || M % v == 0) &&
+    return offsets_fit(lda, ldb, dtype) && rows4_ok(A, lda, B, ldb, dtype, x) && (!ta || M % v == 0) &&
            (tb || N % v == 0);
 }
 

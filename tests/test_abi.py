@@ -253,15 +253,18 @@ def test_fp32_tile_by_rounds():
     # the 4-byte-load kernels follow the same rule (K and N not multiples of 4):
     # 4097 columns end in a partly filled round of the larger tiles.  On the
     # 64x64 tile a k-contiguous operand takes 16-byte loads (nn, tt: 16-deep
-    # slabs; nt: 32-deep); tn, with none, keeps the 4-byte kernel
+    # slabs); tn, with none, keeps the 4-byte kernel; nt (both operands
+    # k-contiguous, rows 4-byte aligned) runs the 16-byte kernel itself
     M, N, K = 4095, 4097, 1031
     for (ta, tb), name in (((0, 0), "f32_64x64_pipe4_kw_mfma32x32x2"), ((1, 1), "f32_64x64_pipe4_kw_mfma32x32x2"),
-                           ((0, 1), "f32_64x64_pipe3_k32_kw_mfma32x32x2"), ((1, 0), "f32_64x64_pipe4_dw_mfma32x32x2")):
+                           ((0, 1), "f32_64x64_pipe3_k32_mfma32x32x2"), ((1, 0), "f32_64x64_pipe4_dw_mfma32x32x2")):
         lda, ldb = (M if ta else K) + 8, (K if tb else N) + 8
         k = dg.dg_select_kernel(ta, tb, M, N, K, 256, lda, 256, ldb, 256, N + 8, 0)
         assert dg.dg_kernel_name(k) == name, (ta, tb)
     k = dg.dg_select_kernel(0, 0, 4096, 4096, 4095, 256, 4095, 256, 4096, 256, 4096, 0)
-    assert dg.dg_kernel_name(k) == "f32_256x128_pipe3_dw_mfma32x32x2"
+    assert dg.dg_kernel_name(k) == "f32_256x128_pipe3_mfma32x32x2"      # 4-byte rows suffice
+    k = dg.dg_select_kernel(0, 0, 4096, 4095, 4095, 256, 4095, 256, 4095, 256, 4096, 0)
+    assert dg.dg_kernel_name(k) == "f32_256x128_pipe3_dw_mfma32x32x2"   # N not a multiple of 4
 
 
 def test_pipelined_kernels_need_32bit_panel_offsets():

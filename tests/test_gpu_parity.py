@@ -33,10 +33,12 @@ def kernels_for(dg, dtype):
 
 
 def pipe_ok(p):
-    """Preconditions of the pipelined kernels: 16-byte rows of A and B, and
+    """Preconditions of the pipelined 16-byte-load kernels: rows of A and B
+    4-byte aligned (the loads sit at 16-byte multiples from a row start), and
     the m/n-contiguous operand's extent a whole number of 16-byte pieces."""
     v = 4 if p.dtype == "f32" else 8
-    return (p.lda % v == 0 and p.ldb % v == 0 and (not p.ta or p.M % v == 0)
+    r = 1 if p.dtype == "f32" else 2
+    return (p.lda % r == 0 and p.ldb % r == 0 and (not p.ta or p.M % v == 0)
             and (p.tb or p.N % v == 0))
 
 
@@ -513,11 +515,12 @@ def _pad_4byte_rows(base, dtype):
 @pytest.mark.parametrize("shape", [(300, 258, 131), (130, 66, 70), (520, 514, 1030)])
 def test_four_byte_direct_loads(dg, dtype, ta, tb, shape):
     """The library's own choice on row strides that rule out 16-byte
-    alignment: a pipelined kernel with 4-byte loads (`_dw`), or for fp32 on
-    the 64x64 tile 16-byte loads of a k-contiguous operand at 4-byte aligned
-    rows (`_kw`), every output against the oracle, alpha/beta applied, C's
-    padding untouched.  Odd K puts a pair of 16-bit elements across the end
-    of K in the last slab."""
+    alignment: the 16-byte-load kernels where the m/n-contiguous extents are
+    whole 16-byte pieces (the loads need 4-byte aligned rows only), else a
+    pipelined kernel with 4-byte loads (`_dw`), or for fp32 on the 64x64 tile
+    16-byte loads of a k-contiguous operand (`_kw`); every output against the
+    oracle, alpha/beta applied, C's padding untouched.  Odd K puts a pair of
+    16-bit elements across the end of K in the last slab."""
     M, N, K = shape
     dist = "uniform" if dtype == "f32" else "normal_sqrtk"
     a, b, c0 = synth.problem(M, N, K, dtype, dist, 540 + M + K, with_c0=True)
@@ -527,7 +530,8 @@ def test_four_byte_direct_loads(dg, dtype, ta, tb, shape):
     k = dg.dg_select_kernel(int(ta), int(tb), M, N, K, 256, p.lda, 256, p.ldb, 256, p.ldc,
                             {"f32": 0, "f16": 1, "bf16": 2}[dtype])
     name = dg.dg_kernel_name(k)
-    assert "_dw_" in name or (dtype == "f32" and "_kw_" in name), name
+    assert "pipe" in name, name
+    assert pipe_ok(p) or "_dw_" in name or (dtype == "f32" and "_kw_" in name), name
     print(f"4-byte loads {dtype} {shape} ta={ta} tb={tb} lda={p.lda} ldb={p.ldb} "
           f"kernel={dg.dg_kernel_name(k)}", flush=True)
     check_full(p, out=p.run_gpu())
